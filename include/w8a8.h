@@ -1,0 +1,129 @@
+/*
+ * w8a8.h — C ABI of the MI355X (gfx950) fused W8A8 linear library, libw8a8.so.
+ *
+ * The operation is the one in the abstract of "Realizing Native INT8 Compute
+ * for Diffusion Transformers on Consumer GPUs: A Fused INT8 GEMM Kernel for
+ * Ideogram 4.0" (arXiv 2606.14598): activations are quantized to int8 per
+ * token, weights per (output) channel, the product is accumulated
+ * int8 x int8 -> int32 on the matrix cores, and the per-token x per-channel
+ * dequantization plus the bias are folded into the GEMM epilogue, which
+ * writes bf16.
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are dense, row-major, in device memory (hipMalloc'd or a
+ *     torch device tensor); bf16 values are passed as their uint16_t bits.
+ *   - X is [M,K] (one row per token), W is [N,K] (one row per output channel,
+ *     the torch nn.Linear layout), Y is [M,N].
+ *   - The caller owns every buffer.  The library allocates no device memory,
+ *     keeps no pointer after returning and holds no mutable state; it is
+ *     thread-safe.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream);
+ *     results are valid once that stream has been synchronised.
+ *   - Arguments are validated before anything is launched; on any error
+ *     nothing is launched and no output byte is written.  Shapes are checked
+ *     first: an empty input (M == 0, or N == 0 for the weight quantizer) is
+ *     then a no-op that returns W8A8_OK without looking at the pointers.
+ *   - Inputs must be finite.  NaN/Inf inputs are outside the contract and not
+ *     checked on the hot path.
+ *   - Shape contract: 16 <= K, K % 16 == 0; N >= 1; M >= 0.  The GEMM entry
+ *     points also require K <= W8A8_MAX_K, the largest K for which a sum of
+ *     K products of codes in [-127, 127] cannot overflow int32.
+ *   - Alignment contract: X, W, Xq and Wq 16-byte aligned; scales 4-byte
+ *     aligned; Y and bias 2-byte aligned; int32 accumulators 4-byte aligned.
+ */
+#ifndef W8A8_H_
+#define W8A8_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* floor((2^31 - 1) / 127^2): sums of this many +-127*127 products fit int32. */
+#define W8A8_MAX_K 133144
+
+typedef enum {
+  W8A8_OK = 0,
+  W8A8_ERR_NULL = 1,   /* a required pointer is NULL */
+  W8A8_ERR_SHAPE = 2,  /* M, N or K outside the shape contract */
+  W8A8_ERR_ALIGN = 3,  /* a pointer breaks the alignment contract */
+  W8A8_ERR_LAUNCH = 4, /* the HIP runtime rejected a launch (wrong device, no device, ...) */
+  W8A8_ERR_ARG = 5     /* any other invalid argument (e.g. an unknown tile id) */
+} w8a8_status;
+
+/* Static, NUL-terminated description of a status code. */
+const char *w8a8_status_str(w8a8_status s);
+
+/*
+ * Per-output-channel weight quantization (offline, once per layer).
+ * For each row n of w [N,K] (bf16 bits):
+ *   amax = max_k |w[n,k]|,  w_scale[n] = fl32(amax / 127),
+ *   wq[n,k] = clamp(rne(fl32(w[n,k] / w_scale[n])), -127, 127),
+ * an all-zero row gives w_scale[n] = 0 and wq[n,:] = 0.
+ * Abstract: weights are quantized and their per-channel scale is folded into
+ * the epilogue.  Outputs: wq int8 [N,K], w_scale fp32 [N].
+ */
+w8a8_status w8a8_quantize_weight(const uint16_t *w, int64_t N, int64_t K,
+                                 int8_t *wq, float *w_scale, hipStream_t stream);
+
+/*
+ * Per-token activation quantization (every forward).  Same row rule as
+ * w8a8_quantize_weight applied to each row m of x [M,K]:
+ * outputs xq int8 [M,K] and x_scale fp32 [M].
+ * Abstract: activations are quantized per token.
+ */
+w8a8_status w8a8_quantize_act(const uint16_t *x, int64_t M, int64_t K,
+                              int8_t *xq, float *x_scale, hipStream_t stream);
+
+/*
+ * Fused W8A8 linear: int8 GEMM with the dequant + bias epilogue.
+ *   acc[m,n] = sum_k xq[m,k] * wq[n,k]                 (exact, int32)
+ *   y[m,n]   = bf16_rne( fl32( fl32( fl32(float(acc[m,n]) * x_scale[m])
+ *                                    * w_scale[n] ) + float(bias[n]) ) )
+ * Each fp32 operation is rounded separately (no fused multiply-add), so y is
+ * a deterministic function of the inputs.  bias may be NULL (treated as 0).
+ * Abstract: int8 x int8 -> int32 on the matrix cores, per-token x per-channel
+ * dequantization and bias folded into the epilogue, bf16 out.
+ * Inputs xq [M,K], x_scale [M], wq [N,K], w_scale [N], bias [N]; output y [M,N].
+ */
+w8a8_status w8a8_linear(const int8_t *xq, const float *x_scale, const int8_t *wq,
+                        const float *w_scale, const uint16_t *bias, uint16_t *y,
+                        int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * Diagnostic entry: the same GEMM main loop, storing the raw int32
+ * accumulators acc [M,N] instead of running the epilogue.
+ * Abstract: the int8 x int8 -> int32 accumulation is checked bit for bit.
+ */
+w8a8_status w8a8_gemm_i32(const int8_t *xq, const int8_t *wq, int32_t *acc,
+                          int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * Per-shape tile selection (the abstract's "autotuned per GEMM shape", here a
+ * fixed table chosen from measurements).  w8a8_num_tiles() is the number of
+ * compiled tile configurations; w8a8_tile_info() describes one (block rows of
+ * X, block rows of W, K bytes per stage, threads; any pointer may be NULL);
+ * w8a8_select_tile() returns the id w8a8_linear would use for a shape.
+ */
+int w8a8_num_tiles(void);
+w8a8_status w8a8_tile_info(int tile, int *block_m, int *block_n, int *block_k, int *threads);
+int w8a8_select_tile(int64_t M, int64_t N, int64_t K);
+
+/*
+ * w8a8_linear / w8a8_gemm_i32 with an explicit tile id (tile < 0 selects as
+ * the plain entry points do).  Every tile gives bit-identical results; these
+ * exist for tests and tile sweeps.  An unknown id returns W8A8_ERR_ARG.
+ */
+w8a8_status w8a8_linear_tile(const int8_t *xq, const float *x_scale, const int8_t *wq,
+                             const float *w_scale, const uint16_t *bias, uint16_t *y,
+                             int64_t M, int64_t N, int64_t K, int tile, hipStream_t stream);
+w8a8_status w8a8_gemm_i32_tile(const int8_t *xq, const int8_t *wq, int32_t *acc,
+                               int64_t M, int64_t N, int64_t K, int tile, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8A8_H_ */

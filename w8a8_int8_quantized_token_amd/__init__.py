@@ -1,0 +1,16 @@
+"""MI355X-native fused W8A8 linear (per-token int8 activations x
+per-output-channel int8 weights -> int32 on the matrix cores -> dequant +
+bias epilogue -> bf16), a thin torch binding over libw8a8.so.
+
+The method is the one in the abstract of "Realizing Native INT8 Compute for
+Diffusion Transformers on Consumer GPUs: A Fused INT8 GEMM Kernel for
+Ideogram 4.0" (arXiv 2606.14598).
+"""
+from ._lib import LIB_PATH, MAX_K, W8A8Error, lib, status_str
+from .module import W8A8Linear
+from .ops import (gemm_i32, linear, num_tiles, quantize_act, quantize_weight, select_tile,
+                  tile_info)
+
+__all__ = ["LIB_PATH", "MAX_K", "W8A8Error", "W8A8Linear", "gemm_i32", "lib", "linear",
+           "num_tiles", "quantize_act", "quantize_weight", "select_tile", "status_str",
+           "tile_info"]

@@ -1,0 +1,57 @@
+"""ctypes loader for libw8a8.so (built in-tree by ``build.py``).
+
+There is no fallback: if the library is missing or does not load, importing
+the package raises, so nothing silently runs on another path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw8a8.so")
+
+# Status codes of include/w8a8.h
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_LAUNCH, ERR_ARG = range(6)
+MAX_K = 133144
+
+
+class W8A8Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m w8a8_int8_quantized_token_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i64, i32, st = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int
+    sig = {
+        "w8a8_status_str": (ctypes.c_char_p, [st]),
+        "w8a8_quantize_weight": (st, [p, i64, i64, p, p, p]),
+        "w8a8_quantize_act": (st, [p, i64, i64, p, p, p]),
+        "w8a8_linear": (st, [p, p, p, p, p, p, i64, i64, i64, p]),
+        "w8a8_gemm_i32": (st, [p, p, p, i64, i64, i64, p]),
+        "w8a8_num_tiles": (i32, []),
+        "w8a8_tile_info": (st, [i32, p, p, p, p]),
+        "w8a8_select_tile": (i32, [i64, i64, i64]),
+        "w8a8_linear_tile": (st, [p, p, p, p, p, p, i64, i64, i64, i32, p]),
+        "w8a8_gemm_i32_tile": (st, [p, p, p, i64, i64, i64, i32, p]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def status_str(status: int) -> str:
+    return lib.w8a8_status_str(status).decode()
+
+
+def check(status: int, where: str) -> None:
+    if status != OK:
+        raise W8A8Error(status, where)

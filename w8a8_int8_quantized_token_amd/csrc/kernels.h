@@ -1,0 +1,36 @@
+// Internal launch interface between the C-ABI layer and the HIP kernels of
+// libw8a8 (gfx950).  Not installed; the public ABI is include/w8a8.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w8a8 {
+
+// Row-wise absmax quantizer: rows of x [R,K] (bf16 bits) -> q int8 [R,K] and
+// scale fp32 [R].  Requires K % 16 == 0 and R > 0.
+hipError_t launch_quantize_rows(const uint16_t* x, int8_t* q, float* scale,
+                                int64_t R, int64_t K, hipStream_t stream);
+
+// One compiled GEMM tile configuration.
+struct TileDesc {
+  int block_m;   // rows of X (tokens) per workgroup
+  int block_n;   // rows of W (output channels) per workgroup
+  int block_k;   // K bytes staged per pipeline step
+  int threads;   // workgroup size
+};
+
+int num_tiles();
+const TileDesc& tile_desc(int tile);
+int select_tile(int64_t M, int64_t N, int64_t K);
+
+enum class Epilogue { kBf16ScaleBias, kRawI32 };
+
+// int8 GEMM acc[m,n] = sum_k xq[m,k] * wq[n,k] with the chosen epilogue.
+// For kBf16ScaleBias `out` is bf16 [M,N] and sx/sw/bias are used (bias may
+// be null); for kRawI32 `out` is int32 [M,N].  Shapes already validated.
+hipError_t launch_gemm(int tile, Epilogue epi, const int8_t* xq, const int8_t* wq,
+                       const float* sx, const float* sw, const uint16_t* bias, void* out,
+                       int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+}  // namespace w8a8

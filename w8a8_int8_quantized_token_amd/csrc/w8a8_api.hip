@@ -1,0 +1,136 @@
+// C ABI of libw8a8: argument validation, tile selection and launches on the
+// caller's stream.  Semantics of each entry point are documented in
+// include/w8a8.h.  Validation always completes before anything is launched.
+#include "../../include/w8a8.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxRows = int64_t(1) << 26;   // M, N limit (grid size)
+constexpr int64_t kMaxQuantK = int64_t(1) << 30;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape first; an empty input is then a no-op whatever the pointers are.
+w8a8_status check_quant(const uint16_t* x, int64_t R, int64_t K, const int8_t* q, const float* s) {
+  if (R < 0 || R > kMaxRows || K < 16 || K % 16 != 0 || K > kMaxQuantK) return W8A8_ERR_SHAPE;
+  if (R == 0) return W8A8_OK;
+  if (!x || !q || !s) return W8A8_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4)) return W8A8_ERR_ALIGN;
+  return W8A8_OK;
+}
+
+w8a8_status quantize(const uint16_t* x, int64_t R, int64_t K, int8_t* q, float* s,
+                     hipStream_t stream) {
+  const w8a8_status st = check_quant(x, R, K, q, s);
+  if (st != W8A8_OK || R == 0) return st;
+  return w8a8::launch_quantize_rows(x, q, s, R, K, stream) == hipSuccess ? W8A8_OK
+                                                                          : W8A8_ERR_LAUNCH;
+}
+
+w8a8_status check_gemm_shape(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || M > kMaxRows || N < 1 || N > kMaxRows || K < 16 || K % 16 != 0 ||
+      K > W8A8_MAX_K)
+    return W8A8_ERR_SHAPE;
+  return W8A8_OK;
+}
+
+w8a8_status check_gemm_ptrs(const int8_t* xq, const int8_t* wq, const void* out) {
+  if (!xq || !wq || !out) return W8A8_ERR_NULL;
+  if (!aligned(xq, 16) || !aligned(wq, 16)) return W8A8_ERR_ALIGN;
+  return W8A8_OK;
+}
+
+int resolve_tile(int tile, int64_t M, int64_t N, int64_t K) {
+  if (tile < 0) return w8a8::select_tile(M, N, K);
+  return tile < w8a8::num_tiles() ? tile : -1;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w8a8_status_str(w8a8_status s) {
+  switch (s) {
+    case W8A8_OK: return "ok";
+    case W8A8_ERR_NULL: return "a required pointer is NULL";
+    case W8A8_ERR_SHAPE: return "shape outside the contract (16 <= K, K % 16 == 0, K <= 133144 for GEMMs, N >= 1, 0 <= M)";
+    case W8A8_ERR_ALIGN: return "pointer breaks the alignment contract";
+    case W8A8_ERR_LAUNCH: return "HIP kernel launch failed";
+    case W8A8_ERR_ARG: return "invalid argument";
+  }
+  return "unknown status";
+}
+
+w8a8_status w8a8_quantize_weight(const uint16_t* w, int64_t N, int64_t K, int8_t* wq,
+                                 float* w_scale, hipStream_t stream) {
+  return quantize(w, N, K, wq, w_scale, stream);
+}
+
+w8a8_status w8a8_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* xq,
+                              float* x_scale, hipStream_t stream) {
+  return quantize(x, M, K, xq, x_scale, stream);
+}
+
+w8a8_status w8a8_linear_tile(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                             const float* w_scale, const uint16_t* bias, uint16_t* y, int64_t M,
+                             int64_t N, int64_t K, int tile, hipStream_t stream) {
+  w8a8_status st = check_gemm_shape(M, N, K);
+  if (st != W8A8_OK) return st;
+  const int t = resolve_tile(tile, M, N, K);
+  if (t < 0) return W8A8_ERR_ARG;
+  if (M == 0) return W8A8_OK;
+  if (!x_scale || !w_scale) return W8A8_ERR_NULL;
+  st = check_gemm_ptrs(xq, wq, y);
+  if (st != W8A8_OK) return st;
+  if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(y, 2) ||
+      (bias && !aligned(bias, 2)))
+    return W8A8_ERR_ALIGN;
+  return w8a8::launch_gemm(t, w8a8::Epilogue::kBf16ScaleBias, xq, wq, x_scale, w_scale, bias, y,
+                           M, N, K, stream) == hipSuccess
+             ? W8A8_OK
+             : W8A8_ERR_LAUNCH;
+}
+
+w8a8_status w8a8_linear(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                        const float* w_scale, const uint16_t* bias, uint16_t* y, int64_t M,
+                        int64_t N, int64_t K, hipStream_t stream) {
+  return w8a8_linear_tile(xq, x_scale, wq, w_scale, bias, y, M, N, K, -1, stream);
+}
+
+w8a8_status w8a8_gemm_i32_tile(const int8_t* xq, const int8_t* wq, int32_t* acc, int64_t M,
+                               int64_t N, int64_t K, int tile, hipStream_t stream) {
+  w8a8_status st = check_gemm_shape(M, N, K);
+  if (st != W8A8_OK) return st;
+  const int t = resolve_tile(tile, M, N, K);
+  if (t < 0) return W8A8_ERR_ARG;
+  if (M == 0) return W8A8_OK;
+  st = check_gemm_ptrs(xq, wq, acc);
+  if (st != W8A8_OK) return st;
+  if (!aligned(acc, 4)) return W8A8_ERR_ALIGN;
+  return w8a8::launch_gemm(t, w8a8::Epilogue::kRawI32, xq, wq, nullptr, nullptr, nullptr, acc, M,
+                           N, K, stream) == hipSuccess
+             ? W8A8_OK
+             : W8A8_ERR_LAUNCH;
+}
+
+w8a8_status w8a8_gemm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc, int64_t M, int64_t N,
+                          int64_t K, hipStream_t stream) {
+  return w8a8_gemm_i32_tile(xq, wq, acc, M, N, K, -1, stream);
+}
+
+int w8a8_num_tiles(void) { return w8a8::num_tiles(); }
+
+w8a8_status w8a8_tile_info(int tile, int* block_m, int* block_n, int* block_k, int* threads) {
+  if (tile < 0 || tile >= w8a8::num_tiles()) return W8A8_ERR_ARG;
+  const w8a8::TileDesc& d = w8a8::tile_desc(tile);
+  if (block_m) *block_m = d.block_m;
+  if (block_n) *block_n = d.block_n;
+  if (block_k) *block_k = d.block_k;
+  if (threads) *threads = d.threads;
+  return W8A8_OK;
+}
+
+int w8a8_select_tile(int64_t M, int64_t N, int64_t K) { return w8a8::select_tile(M, N, K); }
+
+}  // extern "C"

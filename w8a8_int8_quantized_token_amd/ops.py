@@ -1,0 +1,115 @@
+"""Thin torch-facing binding of the C ABI in include/w8a8.h.
+
+Argument marshalling only: dtype / device / contiguity checks, output
+allocation with torch, and the call on the current HIP stream.  Every
+computation runs in libw8a8's HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._lib import check, lib
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: torch.Tensor, dtype, ndim: int, name: str) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D (got shape {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _quant(fn, x: torch.Tensor, q=None, s=None, name="x"):
+    _need(x, torch.bfloat16, 2, name)
+    R, K = x.shape
+    if q is None:
+        q = torch.empty((R, K), dtype=torch.int8, device=x.device)
+    if s is None:
+        s = torch.empty((R,), dtype=torch.float32, device=x.device)
+    _need(q, torch.int8, 2, "q")
+    _need(s, torch.float32, 1, "scale")
+    if tuple(q.shape) != (R, K) or s.shape[0] != R:
+        raise ValueError("output shapes do not match the input")
+    check(fn(x.data_ptr(), R, K, q.data_ptr(), s.data_ptr(), _stream(x)), fn.__name__)
+    return q, s
+
+
+def quantize_weight(w: torch.Tensor, wq=None, w_scale=None):
+    """w bf16 [N,K] -> (wq int8 [N,K], w_scale fp32 [N]), per output channel."""
+    return _quant(lib.w8a8_quantize_weight, w, wq, w_scale, "w")
+
+
+def quantize_act(x: torch.Tensor, xq=None, x_scale=None):
+    """x bf16 [M,K] -> (xq int8 [M,K], x_scale fp32 [M]), per token."""
+    return _quant(lib.w8a8_quantize_act, x, xq, x_scale, "x")
+
+
+def _gemm_args(xq, wq):
+    _need(xq, torch.int8, 2, "xq")
+    _need(wq, torch.int8, 2, "wq")
+    M, K = xq.shape
+    N, K2 = wq.shape
+    if K != K2:
+        raise ValueError(f"K mismatch: xq has {K}, wq has {K2}")
+    return M, N, K
+
+
+def linear(xq, x_scale, wq, w_scale, bias=None, y=None, tile: int = -1):
+    """Fused W8A8 linear: bf16 y [M,N] = dequant(xq @ wq^T) + bias."""
+    M, N, K = _gemm_args(xq, wq)
+    _need(x_scale, torch.float32, 1, "x_scale")
+    _need(w_scale, torch.float32, 1, "w_scale")
+    if x_scale.shape[0] != M or w_scale.shape[0] != N:
+        raise ValueError("scale lengths do not match M / N")
+    bptr = None
+    if bias is not None:
+        _need(bias, torch.bfloat16, 1, "bias")
+        if bias.shape[0] != N:
+            raise ValueError("bias length does not match N")
+        bptr = bias.data_ptr()
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    _need(y, torch.bfloat16, 2, "y")
+    if tuple(y.shape) != (M, N):
+        raise ValueError("y shape does not match [M,N]")
+    check(lib.w8a8_linear_tile(xq.data_ptr(), x_scale.data_ptr(), wq.data_ptr(), w_scale.data_ptr(),
+                               bptr, y.data_ptr(), M, N, K, tile, _stream(xq)), "w8a8_linear")
+    return y
+
+
+def gemm_i32(xq, wq, acc=None, tile: int = -1):
+    """Raw int32 accumulators acc [M,N] = xq @ wq^T (diagnostic)."""
+    M, N, K = _gemm_args(xq, wq)
+    if acc is None:
+        acc = torch.empty((M, N), dtype=torch.int32, device=xq.device)
+    _need(acc, torch.int32, 2, "acc")
+    if tuple(acc.shape) != (M, N):
+        raise ValueError("acc shape does not match [M,N]")
+    check(lib.w8a8_gemm_i32_tile(xq.data_ptr(), wq.data_ptr(), acc.data_ptr(), M, N, K, tile,
+                                 _stream(xq)), "w8a8_gemm_i32")
+    return acc
+
+
+def num_tiles() -> int:
+    return lib.w8a8_num_tiles()
+
+
+def tile_info(tile: int) -> dict:
+    v = [ctypes.c_int() for _ in range(4)]
+    check(lib.w8a8_tile_info(tile, *[ctypes.byref(t) for t in v]), "w8a8_tile_info")
+    return dict(block_m=v[0].value, block_n=v[1].value, block_k=v[2].value, threads=v[3].value)
+
+
+def select_tile(M: int, N: int, K: int) -> int:
+    return lib.w8a8_select_tile(M, N, K)
