@@ -12,15 +12,18 @@
 // four runs of 4 consecutive channels: the epilogue writes 8-byte runs of a
 // row of Y without any transpose.
 //
-// Pipeline: a workgroup owns a BM x BN output tile; K is walked in stages of
-// BK bytes.  Each stage of X and W is fetched with 16-byte global loads into
-// registers, written to one of two LDS buffers (double buffering: the next
-// stage's global loads are in flight while the current stage feeds the
-// MFMAs), and read back with 16-byte LDS reads.  16-byte chunks are XOR
-// swizzled within each LDS row so that the 32 rows a wavefront reads at one
-// K offset fall in distinct banks.  The accumulators (FM x FN tiles of 16
-// int32 per lane) stay in registers for the whole K loop; int32 never
-// touches HBM on the fused path.
+// Pipeline: a workgroup owns a BM x BN output tile and walks K in stages of
+// 64 bytes.  Stages go straight from global memory into a ring of S LDS
+// buffers with buffer_load ... lds (no staging registers, no LDS store
+// instructions); a stage is requested S-1 stages before it is used.  Chunks
+// past K or rows past M/N are requested at an out-of-range buffer offset,
+// which the hardware returns as zeros, so partial tiles need no branches and
+// stages past the end add nothing.  Fragments are read with 16-byte LDS
+// reads, one MFMA K step ahead of the MFMAs that use them, including across
+// the stage boundary.  16-byte chunks are XOR swizzled within each LDS row so
+// that neither the DMA writes nor the fragment reads conflict on banks.  The
+// accumulators stay in registers for the whole K loop; int32 never touches
+// HBM on the fused path.
 //
 // Workgroup order: consecutive workgroup ids are dispatched round robin over
 // the 8 XCDs, each with its own L2.  Ids are remapped so that each XCD gets a
@@ -34,43 +37,57 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWave = 64;
 constexpr int kNumXcd = 8;
 constexpr int kGroupM = 4;
+constexpr int kBK = 64;               // K bytes per stage = bytes per LDS row
+constexpr int kDmaRows = 16;          // one wavefront DMA: 64 lanes x 16 B = 16 rows of 64 B
+constexpr uint32_t kOOB = 0x80000000u;    // buffer offset beyond any tile: reads as zero
+constexpr int kRsrcWord3 = 0x00020000;    // raw buffer, 32-bit data format (gfx9 family)
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int S_>
 struct Tile {
   static constexpr int BM = BM_;  // X rows (tokens) per workgroup
   static constexpr int BN = BN_;  // W rows (output channels) per workgroup
-  static constexpr int BK = BK_;  // K bytes per stage
   static constexpr int WM = WM_;  // wavefronts along M
   static constexpr int WN = WN_;  // wavefronts along N
-  static constexpr int kThreads = WM * WN * kWave;
+  static constexpr int S = S_;    // LDS stages in the ring
+  static constexpr int kWaves = WM * WN;
+  static constexpr int kThreads = kWaves * kWave;
+  static constexpr int BK = kBK;
   static constexpr int TM = BM / WM, TN = BN / WN;   // per-wavefront extent
   static constexpr int FM = TM / 32, FN = TN / 32;   // 32x32 MFMA tiles per wavefront
-  static constexpr int CPR = BK / 16;                // 16-byte chunks per LDS row
-  static constexpr int XCH = BM * CPR / kThreads;    // X chunks per thread per stage
-  static constexpr int WCH = BN * CPR / kThreads;    // W chunks per thread per stage
-  static constexpr int RSTEP = kThreads / CPR;       // rows between a thread's chunks
-  static constexpr int kStageBytes = (BM + BN) * BK;
-  static constexpr int kLdsBytes = 2 * kStageBytes;
+  static constexpr int KSUB = kBK / 32;              // MFMA K steps per stage
+  static constexpr int DX = BM / kDmaRows / kWaves;  // X DMAs per wavefront per stage
+  static constexpr int DW = BN / kDmaRows / kWaves;  // W DMAs per wavefront per stage
+  static constexpr int D = DX + DW;
+  static constexpr int kStageBytes = (BM + BN) * kBK;
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
-  static_assert(BK % 32 == 0 && CPR >= 2 && CPR <= 8, "BK must be 32..128");
-  static_assert(kThreads % CPR == 0, "threads must cover whole rows");
-  static_assert(XCH * kThreads == BM * CPR && WCH * kThreads == BN * CPR, "uneven chunk split");
-  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+  static_assert(DX >= 1 && DW >= 1 && DX * kDmaRows * kWaves == BM && DW * kDmaRows * kWaves == BN,
+                "every wavefront moves whole 16-row blocks of X and W");
+  static_assert(S >= 3 && S <= 4, "ring of 3 or 4 stages");
+  static_assert((S - 2) * D <= 63, "vmcnt range");
+  static_assert(S * kStageBytes <= 160 * 1024, "LDS budget");
 };
 
-// Physical 16-byte chunk of logical chunk c in LDS row r.
-template <int CPR>
-__device__ __forceinline__ int swz(int r, int c) {
-  return c ^ (r & (CPR - 1));
-}
+// Physical 16-byte chunk of logical chunk c in 64-byte LDS row r.  gfx950
+// serves a 16-byte LDS access for 16 lanes at a time out of a 256-byte bank
+// window.  Fragment reads take 16 consecutive rows at one chunk and a DMA
+// writes 4 consecutive rows at every chunk; c ^ ((r >> 2) & 3) puts both sets
+// into 16 distinct 16-byte slots of the window (measured: reads at the
+// linear-access rate, against 1.6x-3x slower without it).
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 2) & 3); }
 
-__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;  // finite inputs
+// One wavefront DMA of 16 bytes per lane from a raw buffer into LDS.  (Kept
+// out of the kernel's lambdas: called from a lambda directly, the builtin
+// keeps the host pass from emitting the kernel's launch stub.)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, int8_t* lds, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, (int)voffset, 0, 0, 0);
 }
 
 __device__ __forceinline__ float bf16_to_float(uint16_t b) {
@@ -82,12 +99,34 @@ __device__ __forceinline__ float dequant(int acc, float sa, float sw, float b) {
   return __fadd_rn(__fmul_rn(__fmul_rn((float)acc, sa), sw), b);
 }
 
+// s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier without a memory fence: every wait it relies on is
+// issued explicitly before it.
+__device__ __forceinline__ void barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <class T, Epilogue EPI>
 __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     const int8_t* __restrict__ X, const int8_t* __restrict__ W, const float* __restrict__ sx,
     const float* __restrict__ sw, const uint16_t* __restrict__ bias, void* __restrict__ out,
     int M, int N, int K, int tiles_m, int tiles_n, int vec_store) {
-  __shared__ __attribute__((aligned(16))) int8_t lds[T::kLdsBytes];
+  // One array per ring slot: distinct objects let the compiler see that a
+  // DMA into one slot never aliases fragment reads from another.
+  __shared__ __attribute__((aligned(16))) int8_t lds0[T::kStageBytes];
+  __shared__ __attribute__((aligned(16))) int8_t lds1[T::kStageBytes];
+  __shared__ __attribute__((aligned(16))) int8_t lds2[T::kStageBytes];
+  __shared__ __attribute__((aligned(16))) int8_t lds3[T::S > 3 ? T::kStageBytes : 16];
+  int8_t* const ring[4] = {lds0, lds1, lds2, lds3};
 
   // ---- workgroup -> output tile (XCD-aware, grouped along M) ----
   const int ntiles = tiles_m * tiles_n;
@@ -104,50 +143,42 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / T::WN, wn = wave % T::WN;
 
-  // ---- global -> register staging addresses (32-bit offsets in the tile) ----
-  const int ld_c = tid % T::CPR;    // chunk column, the same for all of a thread's chunks
-  const int ld_r = tid / T::CPR;    // first row
-  const int8_t* xblk = X + (int64_t)m0 * K;
-  const int8_t* wblk = W + (int64_t)n0 * K;
-  int xoff[T::XCH], woff[T::WCH];
+  // ---- DMA addressing ----
+  // Lane p of a DMA fills LDS slot p of a 16-row block: row p/4, physical
+  // chunk p%4, i.e. logical chunk (p%4) ^ ((row>>2)&3) -- the same column for
+  // every block because blocks start at multiples of 16 rows.
+  const int rows_x = min(T::BM, M - m0), rows_w = min(T::BN, N - n0);
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(X + (int64_t)m0 * K), (short)0, rows_x * K, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(W + (int64_t)n0 * K), (short)0, rows_w * K, kRsrcWord3);
+  const int dma_r = lane / 4;
+  const int dma_k = ((lane % 4) ^ ((lane >> 4) & 3)) * 16;
+  uint32_t xrow[T::DX], wrow[T::DW];   // byte offset of the row start, or kOOB
 #pragma unroll
-  for (int i = 0; i < T::XCH; ++i) {
-    const int r = ld_r + i * T::RSTEP;
-    xoff[i] = (min(m0 + r, M - 1) - m0) * K + ld_c * 16;   // rows past M re-read row M-1
+  for (int i = 0; i < T::DX; ++i) {
+    const int r = (wave + i * T::kWaves) * kDmaRows + dma_r;
+    xrow[i] = r < rows_x ? (uint32_t)(r * K) : kOOB;
   }
 #pragma unroll
-  for (int i = 0; i < T::WCH; ++i) {
-    const int r = ld_r + i * T::RSTEP;
-    woff[i] = (min(n0 + r, N - 1) - n0) * K + ld_c * 16;
+  for (int i = 0; i < T::DW; ++i) {
+    const int r = (wave + i * T::kWaves) * kDmaRows + dma_r;
+    wrow[i] = r < rows_w ? (uint32_t)(r * K) : kOOB;
   }
-  v4i xreg[T::XCH], wreg[T::WCH];
-
-  auto load_stage = [&](int kt) {
-    const int kb = kt * T::BK;
-    const bool ok = kb + ld_c * 16 < K;   // K % 16 == 0: a chunk is all in or all out
+  // Request stage kt into ring slot `buf`; chunks at or past K read as zeros.
+  auto issue = [&](int8_t* buf, int kt) {
+    const int k = kt * kBK + dma_k;
+    const bool kin = k < K;
 #pragma unroll
-    for (int i = 0; i < T::XCH; ++i)
-      xreg[i] = ok ? *reinterpret_cast<const v4i*>(xblk + xoff[i] + kb) : v4i{0, 0, 0, 0};
+    for (int i = 0; i < T::DX; ++i)
+      dma16(rx, buf + (wave + i * T::kWaves) * kDmaRows * kBK, kin ? xrow[i] + (uint32_t)k : kOOB);
 #pragma unroll
-    for (int i = 0; i < T::WCH; ++i)
-      wreg[i] = ok ? *reinterpret_cast<const v4i*>(wblk + woff[i] + kb) : v4i{0, 0, 0, 0};
-  };
-  auto store_stage = [&](int buf) {
-    int8_t* xs = lds + buf * T::kStageBytes;
-    int8_t* ws = xs + T::BM * T::BK;
-#pragma unroll
-    for (int i = 0; i < T::XCH; ++i) {
-      const int r = ld_r + i * T::RSTEP;
-      *reinterpret_cast<v4i*>(xs + r * T::BK + swz<T::CPR>(r, ld_c) * 16) = xreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < T::WCH; ++i) {
-      const int r = ld_r + i * T::RSTEP;
-      *reinterpret_cast<v4i*>(ws + r * T::BK + swz<T::CPR>(r, ld_c) * 16) = wreg[i];
-    }
+    for (int i = 0; i < T::DW; ++i)
+      dma16(rw, buf + T::BM * kBK + (wave + i * T::kWaves) * kDmaRows * kBK,
+            kin ? wrow[i] + (uint32_t)k : kOOB);
   };
 
   v16i acc[T::FM][T::FN];
@@ -158,73 +189,130 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
 
   const int row_in = lane % 32;   // row of the 32-row MFMA operand this lane feeds
   const int khalf = lane / 32;    // which 16-byte half of each 32-byte K step
-  const int KT = (K + T::BK - 1) / T::BK;
 
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const bool more = kt + 1 < KT;
-    if (more) load_stage(kt + 1);
-    const int8_t* xs = lds + (kt & 1) * T::kStageBytes;
-    const int8_t* ws = xs + T::BM * T::BK;
+  // Fragment registers, double buffered by MFMA K step parity.
+  v4i a[2][T::FN], b[2][T::FM];
+  auto frag = [&](const int8_t* buf, int s, int slot) {
+    const int8_t* ws = buf + T::BM * kBK;
+    const int c = s * 2 + khalf;
 #pragma unroll
-    for (int kk = 0; kk < T::BK / 32; ++kk) {
-      const int c = kk * 2 + khalf;
-      v4i a[T::FN], b[T::FM];
-#pragma unroll
-      for (int j = 0; j < T::FN; ++j) {
-        const int r = wn * T::TN + j * 32 + row_in;
-        a[j] = *reinterpret_cast<const v4i*>(ws + r * T::BK + swz<T::CPR>(r, c) * 16);
-      }
-#pragma unroll
-      for (int i = 0; i < T::FM; ++i) {
-        const int r = wm * T::TM + i * 32 + row_in;
-        b[i] = *reinterpret_cast<const v4i*>(xs + r * T::BK + swz<T::CPR>(r, c) * 16);
-      }
-#pragma unroll
-      for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < T::FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[j], b[i], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < T::FN; ++j) {
+      const int r = wn * T::TN + j * 32 + row_in;
+      a[slot][j] = *reinterpret_cast<const v4i*>(ws + r * kBK + swz(r, c) * 16);
     }
-    if (more) store_stage((kt + 1) & 1);
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+      const int r = wm * T::TM + i * 32 + row_in;
+      b[slot][i] = *reinterpret_cast<const v4i*>(buf + r * kBK + swz(r, c) * 16);
+    }
+  };
+  auto mfmas = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[slot][j], b[slot][i], acc[i][j], 0, 0, 0);
+  };
+
+  const int KT = (K + kBK - 1) / kBK;
+  const int KTr = (KT + T::S - 1) / T::S * T::S;   // stages computed (the extra ones are zeros)
+
+  // Step k (stage k in slot `cur`, fragments of its first K step in flight):
+  // request stage k+S-1 into the slot stage k-1 used, run the K steps, then
+  // make stage k+1 visible and start reading its first fragments under the
+  // MFMAs of the last K step.
+  auto step = [&](int8_t* cur, int8_t* nxt, int8_t* freed, int k) {
+    issue(freed, k + T::S - 1);
+#pragma unroll
+    for (int s = 0; s + 1 < T::KSUB; ++s) {
+      frag(cur, s + 1, (s + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(s & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_lgkmcnt0();                 // this wavefront's reads of `cur` are done
+    wait_vmcnt<(T::S - 2) * T::D>();  // its DMAs of stage k+1 have landed
+    barrier();                       // ... and everyone's
+    frag(nxt, 0, T::KSUB & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas((T::KSUB - 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- main loop over a ring of S slots ----
+#pragma unroll
+  for (int s = 0; s + 1 < T::S; ++s) issue(ring[s], s);
+  wait_vmcnt<(T::S - 2) * T::D>();
+  barrier();
+  frag(ring[0], 0, 0);
+  for (int kt = 0; kt < KTr; kt += T::S) {
+    if constexpr (T::S == 3) {
+      step(lds0, lds1, lds2, kt);
+      step(lds1, lds2, lds0, kt + 1);
+      step(lds2, lds0, lds1, kt + 2);
+    } else {
+      step(lds0, lds1, lds3, kt);
+      step(lds1, lds2, lds0, kt + 1);
+      step(lds2, lds3, lds1, kt + 2);
+      step(lds3, lds0, lds2, kt + 3);
+    }
   }
+  wait_vmcnt<0>();
+  wait_lgkmcnt0();
+  barrier();   // every DMA and fragment read is done before LDS is reused
 
   // ---- epilogue: lane holds token m, channels n = base + 8*g + 4*khalf + 0..3 ----
+  if constexpr (EPI == Epilogue::kBf16ScaleBias) {
+    // The block's channel scales and bias (as fp32) go to LDS once, so each
+    // group of 4 outputs needs two 16-byte LDS reads instead of 8 global loads.
+    float* s_lds = reinterpret_cast<float*>(lds0);
+    float* b_lds = s_lds + T::BN;
+    for (int t = tid; t < T::BN; t += T::kThreads) {
+      const int n = n0 + t;
+      s_lds[t] = n < N ? sw[n] : 0.0f;
+      b_lds[t] = (bias != nullptr && n < N) ? bf16_to_float(bias[n]) : 0.0f;
+    }
+    __syncthreads();
 #pragma unroll
-  for (int i = 0; i < T::FM; ++i) {
-    const int m = m0 + wm * T::TM + i * 32 + row_in;
-    if (m >= M) continue;
-    if constexpr (EPI == Epilogue::kBf16ScaleBias) {
+    for (int i = 0; i < T::FM; ++i) {
+      const int m = m0 + wm * T::TM + i * 32 + row_in;
+      if (m >= M) continue;
       uint16_t* yrow = reinterpret_cast<uint16_t*>(out) + (int64_t)m * N;
       const float sa = sx[m];
 #pragma unroll
       for (int j = 0; j < T::FN; ++j) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * T::TN + j * 32 + g * 8 + khalf * 4;
+          const int nl = wn * T::TN + j * 32 + g * 8 + khalf * 4;
+          const int n = n0 + nl;
+          const f32x4 sv = *reinterpret_cast<const f32x4*>(s_lds + nl);
+          const f32x4 bv = *reinterpret_cast<const f32x4*>(b_lds + nl);
+          const v16i& c = acc[i][j];
+          const bf16x2 lo = __builtin_convertvector(
+              (f32x2{dequant(c[g * 4], sa, sv[0], bv[0]), dequant(c[g * 4 + 1], sa, sv[1], bv[1])}),
+              bf16x2);
+          const bf16x2 hi = __builtin_convertvector(
+              (f32x2{dequant(c[g * 4 + 2], sa, sv[2], bv[2]), dequant(c[g * 4 + 3], sa, sv[3], bv[3])}),
+              bf16x2);
+          const uint32_t wlo = __builtin_bit_cast(uint32_t, lo);
+          const uint32_t whi = __builtin_bit_cast(uint32_t, hi);
           if (vec_store && n + 3 < N) {
-            uint32_t h[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float b = bias ? bf16_to_float(bias[n + e]) : 0.0f;
-              h[e] = bf16_rne_bits(dequant(acc[i][j][g * 4 + e], sa, sw[n + e], b));
-            }
-            *reinterpret_cast<u32x2*>(yrow + n) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+            *reinterpret_cast<u32x2*>(yrow + n) = u32x2{wlo, whi};
           } else {
+            const uint16_t h[4] = {(uint16_t)wlo, (uint16_t)(wlo >> 16), (uint16_t)whi,
+                                   (uint16_t)(whi >> 16)};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              if (n + e < N) {
-                const float b = bias ? bf16_to_float(bias[n + e]) : 0.0f;
-                yrow[n + e] = (uint16_t)bf16_rne_bits(dequant(acc[i][j][g * 4 + e], sa, sw[n + e], b));
-              }
-            }
+            for (int e = 0; e < 4; ++e)
+              if (n + e < N) yrow[n + e] = h[e];
           }
         }
       }
-    } else {
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+      const int m = m0 + wm * T::TM + i * 32 + row_in;
+      if (m >= M) continue;
       int32_t* crow = reinterpret_cast<int32_t*>(out) + (int64_t)m * N;
 #pragma unroll
       for (int j = 0; j < T::FN; ++j) {
@@ -267,12 +355,12 @@ hipError_t launch_t(Epilogue epi, const int8_t* xq, const int8_t* wq, const floa
   return hipGetLastError();
 }
 
-using T0 = Tile<256, 256, 64, 2, 2>;
-using T1 = Tile<256, 128, 64, 2, 2>;
-using T2 = Tile<128, 256, 64, 2, 2>;
-using T3 = Tile<128, 128, 64, 2, 2>;
-using T4 = Tile<64, 64, 64, 2, 2>;
-using T5 = Tile<256, 256, 128, 2, 2>;
+using T0 = Tile<256, 256, 2, 4, 4>;
+using T1 = Tile<256, 256, 2, 2, 4>;
+using T2 = Tile<256, 256, 2, 4, 3>;
+using T3 = Tile<256, 128, 2, 2, 4>;
+using T4 = Tile<128, 128, 2, 2, 4>;
+using T5 = Tile<64, 64, 2, 2, 3>;
 
 template <class T>
 constexpr TileDesc desc() { return TileDesc{T::BM, T::BN, T::BK, T::kThreads}; }
@@ -294,9 +382,9 @@ int select_tile(int64_t M, int64_t N, int64_t K) {
            ((N + kTiles[t].block_n - 1) / kTiles[t].block_n);
   };
   if (tiles(0) >= 4 * cus) return 0;
-  if (tiles(1) >= 2 * cus) return 1;
-  if (tiles(3) >= cus) return 3;
-  return 4;
+  if (tiles(3) >= 2 * cus) return 3;
+  if (tiles(4) >= cus) return 4;
+  return 5;
 }
 
 hipError_t launch_gemm(int tile, Epilogue epi, const int8_t* xq, const int8_t* wq,
