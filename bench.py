@@ -1,0 +1,235 @@
+"""Throughput of the fused W8A8 linear on one MI355X.
+
+One step is the whole hot path for the full linear set of a 1024px DiT block
+with classifier-free-guidance batch 2 (8192 tokens): for each of the QKV
+(3072->9216), out (3072->3072), MLP-up (3072->12288) and MLP-down
+(12288->3072) linears, per-token activation quantization of a bf16 input
+followed by the fused int8 GEMM + dequant/bias epilogue that writes bf16.
+Weights are quantized per output channel once, before timing (an offline
+step of the method).  Inputs are seeded synthetic tensors already resident in
+HBM.  `value` is int8 TOPS of the whole step: sum of 2*M*N*K over the four
+linears / step time.
+
+Besides the contract fields the JSON line carries the roofline of the
+dominant kernel (the GEMM, timed per launch with HIP events on its stream),
+the CPU oracle timed on a bounded sample on the host, the quantize kernel's
+HBM rate and a same-shape bf16 torch GEMM on the same GPU.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import datagen  # noqa: E402
+
+WORKLOAD = datagen.WORKLOADS[4]
+MFMA_INT8_PEAK_TOPS = 5000.0   # MI355X dense int8 matrix peak (5.0 POPS)
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+GEMM_SOURCE = os.path.join(ROOT, "w8a8_int8_quantized_token_amd", "csrc", "gemm_i8.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-rows", type=int, default=1024, help="tokens per linear in the CPU sample")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def gemm_traffic():
+    """HBM bytes per GEMM launch measured with rocprofv3 counters, if they were
+    taken on the current kernel source (else None)."""
+    try:
+        rec = json.load(open(PROFILE_TRAFFIC))
+    except (OSError, ValueError):
+        return None
+    digest = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    if rec.get("gemm_source_sha256") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(rows: int) -> dict:
+    """The oracle, as it stands, on the first `rows` tokens of each linear."""
+    import oracle
+    ops = 0
+    elapsed = 0.0
+    for li, shape in enumerate(WORKLOAD.linears):
+        x = datagen.gen_act(shape, WORKLOAD.seed, li, rows=np.arange(rows))
+        w, b = datagen.gen_weight(shape, WORKLOAD.seed, li)
+        wq, ws = oracle.quantize_rows_ref(w)            # offline, not timed
+        oracle.int_gemm_ref(wq[:1], wq[:1])             # load the library outside the clock
+        t0 = time.perf_counter()
+        xq, xs = oracle.quantize_rows_ref(x)
+        acc = oracle.int_gemm_ref(xq, wq)
+        y = oracle.dequant_ref(acc, xs, ws, b)
+        oracle.f32_to_bf16_bits(y)
+        elapsed += time.perf_counter() - t0
+        ops += 2 * rows * shape.N * shape.K
+    threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    return {"value": round(ops / elapsed / 1e12, 4), "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"first {rows} of {WORKLOAD.linears[0].M} tokens of each of the 4 linears "
+                      f"(full N and K), quantize + int32 GEMM + fp32 dequant + bf16; "
+                      f"{ops / 1e9:.1f} G int8 ops in {elapsed:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+                          "(the multi-GPU sharding is described in the design notes, not built)"}))
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    import w8a8_int8_quantized_token_amd as w8
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # ---- inputs, resident in HBM; weights quantized offline ----
+    layers = []
+    for li, shape in enumerate(WORKLOAD.linears):
+        log(f"inputs {shape.name} M={shape.M} K={shape.K} N={shape.N}")
+        x = datagen.gen_act(shape, WORKLOAD.seed, li).to(dev)
+        wbf, b = datagen.gen_weight(shape, WORKLOAD.seed, li)
+        wbf, b = wbf.to(dev), b.to(dev)
+        wq, ws = w8.quantize_weight(wbf)
+        xq = torch.empty((shape.M, shape.K), dtype=torch.int8, device=dev)
+        xs = torch.empty((shape.M,), dtype=torch.float32, device=dev)
+        y = torch.empty((shape.M, shape.N), dtype=torch.bfloat16, device=dev)
+        layers.append(dict(shape=shape, x=x, wbf=wbf, b=b, wq=wq, ws=ws, xq=xq, xs=xs, y=y,
+                           tile=w8.select_tile(shape.M, shape.N, shape.K)))
+    torch.cuda.synchronize()
+    step_ops = WORKLOAD.ops
+
+    nl = len(layers)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+            torch.cuda.Event(enable_timing=True)) for _ in range(nl)] for _ in range(args.steps)]
+
+    def step(events=None):
+        for i, L in enumerate(layers):
+            if events is not None:
+                events[i][0].record(stream)
+            w8.quantize_act(L["x"], L["xq"], L["xs"])
+            if events is not None:
+                events[i][1].record(stream)
+            w8.linear(L["xq"], L["xs"], L["wq"], L["ws"], L["b"], y=L["y"])
+            if events is not None:
+                events[i][2].record(stream)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(ev[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed / args.steps * 1e3
+    value = step_ops * args.steps / elapsed / 1e12
+
+    # per-launch kernel times from the events (the stream the kernels run on)
+    q_ms = np.array([[ev[k][i][0].elapsed_time(ev[k][i][1]) for i in range(nl)] for k in range(args.steps)])
+    g_ms = np.array([[ev[k][i][1].elapsed_time(ev[k][i][2]) for i in range(nl)] for k in range(args.steps)])
+    per = []
+    for i, L in enumerate(layers):
+        s = L["shape"]
+        ops = 2 * s.M * s.N * s.K
+        gm = float(np.mean(g_ms[:, i]))
+        qm = float(np.mean(q_ms[:, i]))
+        per.append({"linear": s.name, "M": s.M, "K": s.K, "N": s.N, "tile": L["tile"],
+                    "gemm_us": round(gm * 1e3, 2), "gemm_tops": round(ops / gm / 1e9, 1),
+                    "quant_us": round(qm * 1e3, 2),
+                    "quant_gbs": round((3 * s.M * s.K + 4 * s.M) / qm / 1e6, 1),
+                    "linear_tops": round(ops / (gm + qm) / 1e9, 1)})
+    gemm_total_ms = float(g_ms.mean(axis=0).sum())
+    gemm_tops = step_ops / gemm_total_ms / 1e9
+    q_bytes = sum(3 * L["shape"].M * L["shape"].K + 4 * L["shape"].M for L in layers)
+    q_total_ms = float(q_ms.mean(axis=0).sum())
+
+    # ---- bf16 comparator: torch F.linear, same shapes, same GPU ----
+    log("bf16 comparator")
+    for L in layers:
+        torch.nn.functional.linear(L["x"], L["wbf"], L["b"])
+    torch.cuda.synchronize()
+    bf_ms = []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for L in layers:
+        ts = []
+        for _ in range(max(3, args.steps // 2)):
+            e0.record(stream)
+            torch.nn.functional.linear(L["x"], L["wbf"], L["b"])
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        bf_ms.append(float(np.median(ts)))
+    bf_total = sum(bf_ms)
+    for p, t in zip(per, bf_ms):
+        p["bf16_us"] = round(t * 1e3, 2)
+
+    traffic = gemm_traffic()
+    roofline = {"bound": "mfma", "kernel": "gemm_i8_kernel (fused W8A8 linear)",
+                "achieved": round(gemm_tops, 1), "peak": MFMA_INT8_PEAK_TOPS, "unit": "TOPS",
+                "frac": round(gemm_tops / MFMA_INT8_PEAK_TOPS, 4), "traffic": traffic,
+                "per_launch": "sum of 2MNK over the four GEMM launches / sum of their mean durations"}
+
+    result = {
+        "metric": "fused W8A8 linear int8 TOPS and % of MI355X int8 MFMA peak; speedup vs bf16",
+        "value": round(value, 1),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD.name, "tokens": WORKLOAD.linears[0].M,
+                   "linears": [f"{L['shape'].name} {L['shape'].K}->{L['shape'].N}" for L in layers],
+                   "ops_per_step": step_ops, "weights": "pre-quantized per output channel",
+                   "inputs": "bf16 N(0,1) activations, N(0,0.02) weights, N(0,0.01) bias, seed 4"},
+        "frac_of_peak": round(value / MFMA_INT8_PEAK_TOPS, 4),
+        "roofline": roofline,
+        "quantize": {"bound": "hbm", "achieved": round(q_bytes / q_total_ms / 1e6, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(q_bytes / q_total_ms / 1e6 / HBM_PEAK_GBS, 4)},
+        "vs_bf16": {"bf16_torch_linear_tops": round(step_ops / bf_total / 1e9, 1),
+                    "speedup_full_linear": round(bf_total / (gemm_total_ms + q_total_ms), 3),
+                    "speedup_gemm_only": round(bf_total / gemm_total_ms, 3)},
+        "per_linear": per,
+    }
+    if not args.no_cpu:
+        log(f"cpu oracle baseline on {args.cpu_rows} tokens per linear")
+        result["cpu_baseline"] = cpu_baseline(args.cpu_rows)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
