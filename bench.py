@@ -47,7 +47,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--cpu-rows", type=int, default=1024, help="tokens per linear in the CPU sample")
+    p.add_argument("--cpu-rows", type=int, default=4096, help="tokens per linear in the CPU sample")
     return p.parse_args()
 
 
