@@ -45,43 +45,49 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kWave = 64;
 constexpr int kNumXcd = 8;
 constexpr int kGroupM = 4;
-constexpr int kBK = 64;               // K bytes per stage = bytes per LDS row
-constexpr int kDmaRows = 16;          // one wavefront DMA: 64 lanes x 16 B = 16 rows of 64 B
+constexpr int kDmaBytes = kWave * 16;    // one wavefront DMA: 64 lanes x 16 B
 constexpr uint32_t kOOB = 0x80000000u;    // buffer offset beyond any tile: reads as zero
 constexpr int kRsrcWord3 = 0x00020000;    // raw buffer, 32-bit data format (gfx9 family)
 
-template <int BM_, int BN_, int WM_, int WN_, int S_>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int S_>
 struct Tile {
   static constexpr int BM = BM_;  // X rows (tokens) per workgroup
   static constexpr int BN = BN_;  // W rows (output channels) per workgroup
+  static constexpr int BK = BK_;  // K bytes per stage = bytes per LDS row
   static constexpr int WM = WM_;  // wavefronts along M
   static constexpr int WN = WN_;  // wavefronts along N
   static constexpr int S = S_;    // LDS stages in the ring
   static constexpr int kWaves = WM * WN;
   static constexpr int kThreads = kWaves * kWave;
-  static constexpr int BK = kBK;
   static constexpr int TM = BM / WM, TN = BN / WN;   // per-wavefront extent
   static constexpr int FM = TM / 32, FN = TN / 32;   // 32x32 MFMA tiles per wavefront
-  static constexpr int KSUB = kBK / 32;              // MFMA K steps per stage
+  static constexpr int KSUB = BK / 32;               // MFMA K steps per stage
+  static constexpr int CPR = BK / 16;                // 16-byte chunks per LDS row
+  static constexpr int kDmaRows = kDmaBytes / BK;    // rows moved by one wavefront DMA
   static constexpr int DX = BM / kDmaRows / kWaves;  // X DMAs per wavefront per stage
   static constexpr int DW = BN / kDmaRows / kWaves;  // W DMAs per wavefront per stage
   static constexpr int D = DX + DW;
-  static constexpr int kStageBytes = (BM + BN) * kBK;
+  static constexpr int kStageBytes = (BM + BN) * BK;
+  static_assert(BK == 64 || BK == 128, "64- or 128-byte stages");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(DX >= 1 && DW >= 1 && DX * kDmaRows * kWaves == BM && DW * kDmaRows * kWaves == BN,
-                "every wavefront moves whole 16-row blocks of X and W");
-  static_assert(S >= 3 && S <= 4, "ring of 3 or 4 stages");
-  static_assert((S - 2) * D <= 63, "vmcnt range");
+                "every wavefront moves whole DMA blocks of X and W");
+  static_assert(S >= 2 && S <= 4, "ring of 2 to 4 stages");
+  static_assert((S - 1) * D <= 63, "vmcnt range");
   static_assert(S * kStageBytes <= 160 * 1024, "LDS budget");
 };
 
-// Physical 16-byte chunk of logical chunk c in 64-byte LDS row r.  gfx950
-// serves a 16-byte LDS access for 16 lanes at a time out of a 256-byte bank
-// window.  Fragment reads take 16 consecutive rows at one chunk and a DMA
-// writes 4 consecutive rows at every chunk; c ^ ((r >> 2) & 3) puts both sets
-// into 16 distinct 16-byte slots of the window (measured: reads at the
-// linear-access rate, against 1.6x-3x slower without it).
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 2) & 3); }
+// Physical 16-byte chunk of logical chunk c in LDS row r (CPR chunks per
+// row).  gfx950 serves a 16-byte LDS access for 16 lanes at a time out of a
+// 256-byte bank window.  Fragment reads take 16 consecutive rows at one chunk
+// and a DMA writes 256/(16*CPR) consecutive rows at every chunk; the XOR puts
+// both sets into 16 distinct 16-byte slots of the window (measured: reads at
+// the linear-access rate, against 1.6x-3x slower without it).
+template <int CPR>
+__device__ __forceinline__ int swz(int r, int c) {
+  if constexpr (CPR == 4) return c ^ ((r >> 2) & 3);
+  else return c ^ ((r >> 1) & 7);
+}
 
 // One wavefront DMA of 16 bytes per lane from a raw buffer into LDS.  (Kept
 // out of the kernel's lambdas: called from a lambda directly, the builtin
@@ -124,8 +130,9 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
   // DMA into one slot never aliases fragment reads from another.
   __shared__ __attribute__((aligned(16))) int8_t lds0[T::kStageBytes];
   __shared__ __attribute__((aligned(16))) int8_t lds1[T::kStageBytes];
-  __shared__ __attribute__((aligned(16))) int8_t lds2[T::kStageBytes];
+  __shared__ __attribute__((aligned(16))) int8_t lds2[T::S > 2 ? T::kStageBytes : 16];
   __shared__ __attribute__((aligned(16))) int8_t lds3[T::S > 3 ? T::kStageBytes : 16];
+  __shared__ __attribute__((aligned(16))) float sbias[EPI == Epilogue::kBf16ScaleBias ? 2 * T::BN : 4];
   int8_t* const ring[4] = {lds0, lds1, lds2, lds3};
 
   // ---- workgroup -> output tile (XCD-aware, grouped along M) ----
@@ -147,38 +154,40 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
   const int wm = wave / T::WN, wn = wave % T::WN;
 
   // ---- DMA addressing ----
-  // Lane p of a DMA fills LDS slot p of a 16-row block: row p/4, physical
-  // chunk p%4, i.e. logical chunk (p%4) ^ ((row>>2)&3) -- the same column for
-  // every block because blocks start at multiples of 16 rows.
+  // Lane p of a DMA fills LDS slot p of a block of kDmaRows rows (DMA writes
+  // are linear, hence conflict-free): row r = block*kDmaRows + p/CPR,
+  // physical chunk p%CPR, so the lane fetches logical chunk swz(r, p%CPR).
   const int rows_x = min(T::BM, M - m0), rows_w = min(T::BN, N - n0);
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(X + (int64_t)m0 * K), (short)0, rows_x * K, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(W + (int64_t)n0 * K), (short)0, rows_w * K, kRsrcWord3);
-  const int dma_r = lane / 4;
-  const int dma_k = ((lane % 4) ^ ((lane >> 4) & 3)) * 16;
-  uint32_t xrow[T::DX], wrow[T::DW];   // byte offset of the row start, or kOOB
+  const int dma_r = lane / T::CPR;
+  int xcol[T::DX], wcol[T::DW];        // K byte offset of the lane's chunk in a stage
+  uint32_t xrow[T::DX], wrow[T::DW];   // byte offset of that chunk in stage 0, or kOOB
 #pragma unroll
   for (int i = 0; i < T::DX; ++i) {
-    const int r = (wave + i * T::kWaves) * kDmaRows + dma_r;
-    xrow[i] = r < rows_x ? (uint32_t)(r * K) : kOOB;
+    const int r = (wave + i * T::kWaves) * T::kDmaRows + dma_r;
+    xcol[i] = swz<T::CPR>(r, lane % T::CPR) * 16;
+    xrow[i] = r < rows_x ? (uint32_t)(r * K + xcol[i]) : kOOB;
   }
 #pragma unroll
   for (int i = 0; i < T::DW; ++i) {
-    const int r = (wave + i * T::kWaves) * kDmaRows + dma_r;
-    wrow[i] = r < rows_w ? (uint32_t)(r * K) : kOOB;
+    const int r = (wave + i * T::kWaves) * T::kDmaRows + dma_r;
+    wcol[i] = swz<T::CPR>(r, lane % T::CPR) * 16;
+    wrow[i] = r < rows_w ? (uint32_t)(r * K + wcol[i]) : kOOB;
   }
   // Request stage kt into ring slot `buf`; chunks at or past K read as zeros.
   auto issue = [&](int8_t* buf, int kt) {
-    const int k = kt * kBK + dma_k;
-    const bool kin = k < K;
+    const int kb = kt * T::BK;
 #pragma unroll
     for (int i = 0; i < T::DX; ++i)
-      dma16(rx, buf + (wave + i * T::kWaves) * kDmaRows * kBK, kin ? xrow[i] + (uint32_t)k : kOOB);
+      dma16(rx, buf + (wave + i * T::kWaves) * kDmaBytes,
+            kb + xcol[i] < K ? xrow[i] + (uint32_t)kb : kOOB);
 #pragma unroll
     for (int i = 0; i < T::DW; ++i)
-      dma16(rw, buf + T::BM * kBK + (wave + i * T::kWaves) * kDmaRows * kBK,
-            kin ? wrow[i] + (uint32_t)k : kOOB);
+      dma16(rw, buf + T::BM * T::BK + (wave + i * T::kWaves) * kDmaBytes,
+            kb + wcol[i] < K ? wrow[i] + (uint32_t)kb : kOOB);
   };
 
   v16i acc[T::FM][T::FN];
@@ -190,20 +199,33 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
   const int row_in = lane % 32;   // row of the 32-row MFMA operand this lane feeds
   const int khalf = lane / 32;    // which 16-byte half of each 32-byte K step
 
+  // The epilogue's scales and bias are requested now, ahead of the stage
+  // DMAs, so their latency is hidden by the K loop (the in-order vector memory
+  // counter keeps the DMA waits below exact).
+  float sa_pre[T::FM], sw_pre = 0.0f, b_pre = 0.0f;
+  if constexpr (EPI == Epilogue::kBf16ScaleBias) {
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) sa_pre[i] = sx[min(m0 + wm * T::TM + i * 32 + row_in, M - 1)];
+    if (tid < T::BN && n0 + tid < N) {
+      sw_pre = sw[n0 + tid];
+      if (bias != nullptr) b_pre = bf16_to_float(bias[n0 + tid]);
+    }
+  }
+
   // Fragment registers, double buffered by MFMA K step parity.
   v4i a[2][T::FN], b[2][T::FM];
   auto frag = [&](const int8_t* buf, int s, int slot) {
-    const int8_t* ws = buf + T::BM * kBK;
+    const int8_t* ws = buf + T::BM * T::BK;
     const int c = s * 2 + khalf;
 #pragma unroll
     for (int j = 0; j < T::FN; ++j) {
       const int r = wn * T::TN + j * 32 + row_in;
-      a[slot][j] = *reinterpret_cast<const v4i*>(ws + r * kBK + swz(r, c) * 16);
+      a[slot][j] = *reinterpret_cast<const v4i*>(ws + r * T::BK + swz<T::CPR>(r, c) * 16);
     }
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
       const int r = wm * T::TM + i * 32 + row_in;
-      b[slot][i] = *reinterpret_cast<const v4i*>(buf + r * kBK + swz(r, c) * 16);
+      b[slot][i] = *reinterpret_cast<const v4i*>(buf + r * T::BK + swz<T::CPR>(r, c) * 16);
     }
   };
   auto mfmas = [&](int slot) {
@@ -214,15 +236,15 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
         acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[slot][j], b[slot][i], acc[i][j], 0, 0, 0);
   };
 
-  const int KT = (K + kBK - 1) / kBK;
+  const int KT = (K + T::BK - 1) / T::BK;
   const int KTr = (KT + T::S - 1) / T::S * T::S;   // stages computed (the extra ones are zeros)
 
   // Step k (stage k in slot `cur`, fragments of its first K step in flight):
-  // request stage k+S-1 into the slot stage k-1 used, run the K steps, then
-  // make stage k+1 visible and start reading its first fragments under the
-  // MFMAs of the last K step.
-  auto step = [&](int8_t* cur, int8_t* nxt, int8_t* freed, int k) {
-    issue(freed, k + T::S - 1);
+  // run the K steps; once every wavefront is past its reads of `cur` and
+  // stage k+1 has landed (one barrier), request stage k+S into `cur` and
+  // start reading stage k+1's first fragments under the MFMAs of the last K
+  // step.  A stage is thus requested a full S-1 steps before it is needed.
+  auto step = [&](int8_t* cur, int8_t* nxt, int k) {
 #pragma unroll
     for (int s = 0; s + 1 < T::KSUB; ++s) {
       frag(cur, s + 1, (s + 1) & 1);
@@ -233,6 +255,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     wait_lgkmcnt0();                 // this wavefront's reads of `cur` are done
     wait_vmcnt<(T::S - 2) * T::D>();  // its DMAs of stage k+1 have landed
     barrier();                       // ... and everyone's
+    issue(cur, k + T::S);
     frag(nxt, 0, T::KSUB & 1);
     __builtin_amdgcn_sched_barrier(0);
     mfmas((T::KSUB - 1) & 1);
@@ -241,20 +264,23 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
 
   // ---- main loop over a ring of S slots ----
 #pragma unroll
-  for (int s = 0; s + 1 < T::S; ++s) issue(ring[s], s);
-  wait_vmcnt<(T::S - 2) * T::D>();
+  for (int s = 0; s < T::S; ++s) issue(ring[s], s);
+  wait_vmcnt<(T::S - 1) * T::D>();
   barrier();
   frag(ring[0], 0, 0);
   for (int kt = 0; kt < KTr; kt += T::S) {
-    if constexpr (T::S == 3) {
-      step(lds0, lds1, lds2, kt);
-      step(lds1, lds2, lds0, kt + 1);
-      step(lds2, lds0, lds1, kt + 2);
+    if constexpr (T::S == 2) {
+      step(lds0, lds1, kt);
+      step(lds1, lds0, kt + 1);
+    } else if constexpr (T::S == 3) {
+      step(lds0, lds1, kt);
+      step(lds1, lds2, kt + 1);
+      step(lds2, lds0, kt + 2);
     } else {
-      step(lds0, lds1, lds3, kt);
-      step(lds1, lds2, lds0, kt + 1);
-      step(lds2, lds3, lds1, kt + 2);
-      step(lds3, lds0, lds2, kt + 3);
+      step(lds0, lds1, kt);
+      step(lds1, lds2, kt + 1);
+      step(lds2, lds3, kt + 2);
+      step(lds3, lds0, kt + 3);
     }
   }
   wait_vmcnt<0>();
@@ -265,40 +291,80 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
   if constexpr (EPI == Epilogue::kBf16ScaleBias) {
     // The block's channel scales and bias (as fp32) go to LDS once, so each
     // group of 4 outputs needs two 16-byte LDS reads instead of 8 global loads.
-    float* s_lds = reinterpret_cast<float*>(lds0);
-    float* b_lds = s_lds + T::BN;
-    for (int t = tid; t < T::BN; t += T::kThreads) {
-      const int n = n0 + t;
-      s_lds[t] = n < N ? sw[n] : 0.0f;
-      b_lds[t] = (bias != nullptr && n < N) ? bf16_to_float(bias[n]) : 0.0f;
+    float* s_lds = sbias;
+    float* b_lds = sbias + T::BN;
+    static_assert(T::BN <= T::kThreads, "one thread per channel of the block");
+    if (tid < T::BN) {
+      s_lds[tid] = sw_pre;
+      b_lds[tid] = b_pre;
     }
     __syncthreads();
+    // 4 bf16 outputs (two packed words) of MFMA tile (i, j), run g.
+    auto outputs = [&](int i, int j, int g, float sa, uint32_t& wlo, uint32_t& whi) {
+      const int nl = wn * T::TN + j * 32 + g * 8 + khalf * 4;
+      const f32x4 sv = *reinterpret_cast<const f32x4*>(s_lds + nl);
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(b_lds + nl);
+      const v16i& c = acc[i][j];
+      const bf16x2 lo = __builtin_convertvector(
+          (f32x2{dequant(c[g * 4], sa, sv[0], bv[0]), dequant(c[g * 4 + 1], sa, sv[1], bv[1])}), bf16x2);
+      const bf16x2 hi = __builtin_convertvector(
+          (f32x2{dequant(c[g * 4 + 2], sa, sv[2], bv[2]), dequant(c[g * 4 + 3], sa, sv[3], bv[3])}), bf16x2);
+      wlo = __builtin_bit_cast(uint32_t, lo);
+      whi = __builtin_bit_cast(uint32_t, hi);
+    };
+    if (vec_store) {
+      // Row-major Y with N % 8 == 0: each wavefront turns 32 rows x TN of its
+      // results around in its own LDS region and writes whole 16-byte row
+      // chunks, so a store instruction covers full 128-byte lines instead of
+      // 32 scattered 16-byte pieces.
+      constexpr int RB = T::TN * 2;                   // bytes per region row
+      constexpr int RCH = RB / 16;                    // 16-byte chunks per region row
+      constexpr int RWIN = RB >= 256 ? 1 : 256 / RB;  // region rows per 256-byte bank window
+      constexpr int RPI = kDmaBytes / RB;             // rows per wavefront store
+      static_assert(T::kWaves * 32 * RB <= T::kStageBytes, "regions fit in one ring slot");
+      int8_t* region = lds0 + wave * 32 * RB;
+      auto rsw = [](int r, int c) { return c ^ ((r / RWIN) & (RCH - 1)); };
+      const int n = n0 + wn * T::TN + (lane % RCH) * 8;   // this lane's 8 channels when storing
 #pragma unroll
-    for (int i = 0; i < T::FM; ++i) {
-      const int m = m0 + wm * T::TM + i * 32 + row_in;
-      if (m >= M) continue;
-      uint16_t* yrow = reinterpret_cast<uint16_t*>(out) + (int64_t)m * N;
-      const float sa = sx[m];
+      for (int i = 0; i < T::FM; ++i) {
+        const int mb = m0 + wm * T::TM + i * 32;
 #pragma unroll
-      for (int j = 0; j < T::FN; ++j) {
+        for (int j = 0; j < T::FN; ++j) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int nl = wn * T::TN + j * 32 + g * 8 + khalf * 4;
-          const int n = n0 + nl;
-          const f32x4 sv = *reinterpret_cast<const f32x4*>(s_lds + nl);
-          const f32x4 bv = *reinterpret_cast<const f32x4*>(b_lds + nl);
-          const v16i& c = acc[i][j];
-          const bf16x2 lo = __builtin_convertvector(
-              (f32x2{dequant(c[g * 4], sa, sv[0], bv[0]), dequant(c[g * 4 + 1], sa, sv[1], bv[1])}),
-              bf16x2);
-          const bf16x2 hi = __builtin_convertvector(
-              (f32x2{dequant(c[g * 4 + 2], sa, sv[2], bv[2]), dequant(c[g * 4 + 3], sa, sv[3], bv[3])}),
-              bf16x2);
-          const uint32_t wlo = __builtin_bit_cast(uint32_t, lo);
-          const uint32_t whi = __builtin_bit_cast(uint32_t, hi);
-          if (vec_store && n + 3 < N) {
-            *reinterpret_cast<u32x2*>(yrow + n) = u32x2{wlo, whi};
-          } else {
+          for (int g = 0; g < 4; ++g) {
+            uint32_t wlo, whi;
+            outputs(i, j, g, sa_pre[i], wlo, whi);
+            *reinterpret_cast<u32x2*>(region + row_in * RB + rsw(row_in, 4 * j + g) * 16 + 8 * khalf) =
+                u32x2{wlo, whi};
+          }
+        }
+        v4i v[32 / RPI];
+#pragma unroll
+        for (int it = 0; it < 32 / RPI; ++it) {
+          const int r = it * RPI + lane / RCH;
+          v[it] = *reinterpret_cast<const v4i*>(region + r * RB + rsw(r, lane % RCH) * 16);
+        }
+#pragma unroll
+        for (int it = 0; it < 32 / RPI; ++it) {
+          const int m = mb + it * RPI + lane / RCH;
+          if (m < M && n < N)
+            *reinterpret_cast<v4i*>(reinterpret_cast<uint16_t*>(out) + (int64_t)m * N + n) = v[it];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i) {
+        const int m = m0 + wm * T::TM + i * 32 + row_in;
+        if (m >= M) continue;
+        uint16_t* yrow = reinterpret_cast<uint16_t*>(out) + (int64_t)m * N;
+        const float sa = sa_pre[i];
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            uint32_t wlo, whi;
+            outputs(i, j, g, sa, wlo, whi);
+            const int n = n0 + wn * T::TN + j * 32 + g * 8 + khalf * 4;
             const uint16_t h[4] = {(uint16_t)wlo, (uint16_t)(wlo >> 16), (uint16_t)whi,
                                    (uint16_t)(whi >> 16)};
 #pragma unroll
@@ -343,7 +409,7 @@ hipError_t launch_t(Epilogue epi, const int8_t* xq, const int8_t* wq, const floa
   const dim3 block(T::kThreads);
   const uintptr_t o = reinterpret_cast<uintptr_t>(out);
   if (epi == Epilogue::kBf16ScaleBias) {
-    const int vec = (N % 4 == 0) && (o % 8 == 0);
+    const int vec = (N % 8 == 0) && (o % 16 == 0);
     hipLaunchKernelGGL((gemm_i8_kernel<T, Epilogue::kBf16ScaleBias>), grid, block, 0, stream, xq,
                        wq, sx, sw, bias, out, (int)M, (int)N, (int)K, tiles_m, tiles_n, vec);
   } else {
@@ -355,12 +421,12 @@ hipError_t launch_t(Epilogue epi, const int8_t* xq, const int8_t* wq, const floa
   return hipGetLastError();
 }
 
-using T0 = Tile<256, 256, 2, 4, 4>;
-using T1 = Tile<256, 256, 2, 2, 4>;
-using T2 = Tile<256, 256, 2, 4, 3>;
-using T3 = Tile<256, 128, 2, 2, 4>;
-using T4 = Tile<128, 128, 2, 2, 4>;
-using T5 = Tile<64, 64, 2, 2, 3>;
+using T0 = Tile<256, 256, 64, 2, 4, 4>;
+using T1 = Tile<256, 256, 128, 2, 4, 2>;
+using T2 = Tile<256, 256, 64, 2, 4, 3>;
+using T3 = Tile<256, 128, 128, 2, 2, 3>;
+using T4 = Tile<128, 128, 64, 2, 2, 4>;
+using T5 = Tile<64, 64, 64, 2, 2, 3>;
 
 template <class T>
 constexpr TileDesc desc() { return TileDesc{T::BM, T::BN, T::BK, T::kThreads}; }
@@ -373,7 +439,10 @@ constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 int num_tiles() { return kNumTiles; }
 const TileDesc& tile_desc(int tile) { return kTiles[tile]; }
 
-// Shape -> tile.  Prefer the largest tile that still gives every CU work.
+// Shape -> tile, from sweeps of every tile over the DiT shapes on MI355X:
+// 256x256 tiles with 128-byte stages win whenever they give every CU at
+// least one tile; below that, 256x128, then 128x128, then 64x64 tiles keep
+// the 256 CUs busy.
 int select_tile(int64_t M, int64_t N, int64_t K) {
   (void)K;
   const int64_t cus = 256;
@@ -381,9 +450,9 @@ int select_tile(int64_t M, int64_t N, int64_t K) {
     return ((M + kTiles[t].block_m - 1) / kTiles[t].block_m) *
            ((N + kTiles[t].block_n - 1) / kTiles[t].block_n);
   };
-  if (tiles(0) >= 4 * cus) return 0;
-  if (tiles(3) >= 2 * cus) return 3;
-  if (tiles(4) >= cus) return 4;
+  if (tiles(1) >= cus) return 1;
+  if (tiles(3) >= cus / 2) return 3;
+  if (tiles(4) >= cus / 2) return 4;
   return 5;
 }
 
