@@ -49,6 +49,9 @@ constexpr int kDmaBytes = kWave * 16;    // one wavefront DMA: 64 lanes x 16 B
 constexpr uint32_t kOOB = 0x80000000u;    // buffer offset beyond any tile: reads as zero
 constexpr int kRsrcWord3 = 0x00020000;    // raw buffer, 32-bit data format (gfx9 family)
 
+// S >= 2: ring of S whole stages.  S == 0: split ring -- three X slots and
+// two W slots of BM x BK bytes each, so X is requested two stages ahead and
+// W one (see the main loop).
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int S_>
 struct Tile {
   static constexpr int BM = BM_;  // X rows (tokens) per workgroup
@@ -56,7 +59,8 @@ struct Tile {
   static constexpr int BK = BK_;  // K bytes per stage = bytes per LDS row
   static constexpr int WM = WM_;  // wavefronts along M
   static constexpr int WN = WN_;  // wavefronts along N
-  static constexpr int S = S_;    // LDS stages in the ring
+  static constexpr bool kSplit = S_ == 0;
+  static constexpr int S = kSplit ? 2 : S_;   // whole stages in the ring (split: see above)
   static constexpr int kWaves = WM * WN;
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int TM = BM / WM, TN = BN / WN;   // per-wavefront extent
@@ -68,13 +72,16 @@ struct Tile {
   static constexpr int DW = BN / kDmaRows / kWaves;  // W DMAs per wavefront per stage
   static constexpr int D = DX + DW;
   static constexpr int kStageBytes = (BM + BN) * BK;
+  static constexpr int kSlotBytes = kSplit ? BM * BK : kStageBytes;   // bytes per LDS array
+  static constexpr int kSlots = kSplit ? 5 : S;
   static_assert(BK == 64 || BK == 128, "64- or 128-byte stages");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(DX >= 1 && DW >= 1 && DX * kDmaRows * kWaves == BM && DW * kDmaRows * kWaves == BN,
                 "every wavefront moves whole DMA blocks of X and W");
   static_assert(S >= 2 && S <= 4, "ring of 2 to 4 stages");
   static_assert((S - 1) * D <= 63, "vmcnt range");
-  static_assert(S * kStageBytes <= 160 * 1024, "LDS budget");
+  static_assert(!kSplit || BM == BN, "split ring slots hold X or W");
+  static_assert(kSlots * kSlotBytes <= 160 * 1024, "LDS budget");
 };
 
 // Physical 16-byte chunk of logical chunk c in LDS row r (CPR chunks per
@@ -128,11 +135,11 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     int M, int N, int K, int tiles_m, int tiles_n, int vec_store) {
   // One array per ring slot: distinct objects let the compiler see that a
   // DMA into one slot never aliases fragment reads from another.
-  __shared__ __attribute__((aligned(16))) int8_t lds0[T::kStageBytes];
-  __shared__ __attribute__((aligned(16))) int8_t lds1[T::kStageBytes];
-  __shared__ __attribute__((aligned(16))) int8_t lds2[T::S > 2 ? T::kStageBytes : 16];
-  __shared__ __attribute__((aligned(16))) int8_t lds3[T::S > 3 ? T::kStageBytes : 16];
-  __shared__ __attribute__((aligned(16))) float sbias[EPI == Epilogue::kBf16ScaleBias ? 2 * T::BN : 4];
+  __shared__ __attribute__((aligned(16))) int8_t lds0[T::kSlotBytes];
+  __shared__ __attribute__((aligned(16))) int8_t lds1[T::kSlotBytes];
+  __shared__ __attribute__((aligned(16))) int8_t lds2[T::kSlots > 2 ? T::kSlotBytes : 16];
+  __shared__ __attribute__((aligned(16))) int8_t lds3[T::kSlots > 3 ? T::kSlotBytes : 16];
+  __shared__ __attribute__((aligned(16))) int8_t lds4[T::kSlots > 4 ? T::kSlotBytes : 16];
   int8_t* const ring[4] = {lds0, lds1, lds2, lds3};
 
   // ---- workgroup -> output tile (XCD-aware, grouped along M) ----
@@ -177,17 +184,26 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     wcol[i] = swz<T::CPR>(r, lane % T::CPR) * 16;
     wrow[i] = r < rows_w ? (uint32_t)(r * K + wcol[i]) : kOOB;
   }
-  // Request stage kt into ring slot `buf`; chunks at or past K read as zeros.
-  auto issue = [&](int8_t* buf, int kt) {
+  // Request the X (W) part of stage kt into `buf`; chunks at or past K read
+  // as zeros.
+  auto issue_x = [&](int8_t* buf, int kt) {
     const int kb = kt * T::BK;
 #pragma unroll
     for (int i = 0; i < T::DX; ++i)
       dma16(rx, buf + (wave + i * T::kWaves) * kDmaBytes,
             kb + xcol[i] < K ? xrow[i] + (uint32_t)kb : kOOB);
+  };
+  auto issue_w = [&](int8_t* buf, int kt) {
+    const int kb = kt * T::BK;
 #pragma unroll
     for (int i = 0; i < T::DW; ++i)
-      dma16(rw, buf + T::BM * T::BK + (wave + i * T::kWaves) * kDmaBytes,
+      dma16(rw, buf + (wave + i * T::kWaves) * kDmaBytes,
             kb + wcol[i] < K ? wrow[i] + (uint32_t)kb : kOOB);
+  };
+  // Whole stage kt into ring slot `buf` (X rows first, then W rows).
+  auto issue = [&](int8_t* buf, int kt) {
+    issue_x(buf, kt);
+    issue_w(buf + T::BM * T::BK, kt);
   };
 
   v16i acc[T::FM][T::FN];
@@ -214,8 +230,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
 
   // Fragment registers, double buffered by MFMA K step parity.
   v4i a[2][T::FN], b[2][T::FM];
-  auto frag = [&](const int8_t* buf, int s, int slot) {
-    const int8_t* ws = buf + T::BM * T::BK;
+  auto frag2 = [&](const int8_t* xs, const int8_t* ws, int s, int slot) {
     const int c = s * 2 + khalf;
 #pragma unroll
     for (int j = 0; j < T::FN; ++j) {
@@ -225,15 +240,30 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
       const int r = wm * T::TM + i * 32 + row_in;
-      b[slot][i] = *reinterpret_cast<const v4i*>(buf + r * T::BK + swz<T::CPR>(r, c) * 16);
+      b[slot][i] = *reinterpret_cast<const v4i*>(xs + r * T::BK + swz<T::CPR>(r, c) * 16);
     }
   };
+  auto frag = [&](const int8_t* buf, int s, int slot) { frag2(buf, buf + T::BM * T::BK, s, slot); };
   auto mfmas = [&](int slot) {
 #pragma unroll
     for (int i = 0; i < T::FM; ++i)
 #pragma unroll
       for (int j = 0; j < T::FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[slot][j], b[slot][i], acc[i][j], 0, 0, 0);
+  };
+
+  // Scheduling of the code after a barrier: the next stage's first fragment
+  // reads, then the last K step's MFMAs each followed by one stage request
+  // (and its address arithmetic), so the MFMA pipe restarts right away.
+  auto interleave = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, T::FM + T::FN, 0);   // fragment reads
+#pragma unroll
+    for (int q = 0; q < T::FM * T::FN; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);             // address VALU
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);             // one DMA
+    }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   const int KT = (K + T::BK - 1) / T::BK;
@@ -255,32 +285,79 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     wait_lgkmcnt0();                 // this wavefront's reads of `cur` are done
     wait_vmcnt<(T::S - 2) * T::D>();  // its DMAs of stage k+1 have landed
     barrier();                       // ... and everyone's
-    issue(cur, k + T::S);
     frag(nxt, 0, T::KSUB & 1);
-    __builtin_amdgcn_sched_barrier(0);
+    issue(cur, k + T::S);
     mfmas((T::KSUB - 1) & 1);
-    __builtin_amdgcn_sched_barrier(0);
+    interleave();
+  };
+
+  // Split-ring step k: X_k in `xc`, W_k in `wc`, stage k+1 in `xn`/`wn1`.
+  // After the barrier that frees X_k's and W_k's slots, W_{k+2} and then
+  // X_{k+3} are requested into them: at the next barrier only the W part
+  // (half a stage, requested one step earlier) is on the critical path, while
+  // X has two steps to land.
+  auto step_split = [&](int8_t* xc, int8_t* wc, int8_t* xn, int8_t* wn1, int k) {
+#pragma unroll
+    for (int s = 0; s + 1 < T::KSUB; ++s) {
+      frag2(xc, wc, s + 1, (s + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(s & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_lgkmcnt0();
+    wait_vmcnt<T::DX>();   // everything but X_{k+2} (the last request) has landed
+    barrier();
+    // After the barrier: the next stage's first fragment reads, the last K
+    // step's MFMAs and the next requests, interleaved so that the MFMA pipe
+    // restarts right away instead of waiting for the DMA issue.
+    frag2(xn, wn1, 0, T::KSUB & 1);
+    issue_w(wc, k + 2);
+    issue_x(xc, k + 3);
+    mfmas((T::KSUB - 1) & 1);
+    interleave();
   };
 
   // ---- main loop over a ring of S slots ----
+  if constexpr (T::kSplit) {
+    // X slots lds0..lds2 (X_k in slot k%3), W slots lds3, lds4 (W_k in k%2);
+    // the slot pattern repeats every 6 stages.
+    issue_x(lds0, 0);
+    issue_w(lds3, 0);
+    issue_x(lds1, 1);
+    issue_w(lds4, 1);
+    issue_x(lds2, 2);
+    wait_vmcnt<2 * T::DX + T::DW>();
+    barrier();
+    frag2(lds0, lds3, 0, 0);
+    const int KT6 = (KT + 5) / 6 * 6;
+    for (int kt = 0; kt < KT6; kt += 6) {
+      step_split(lds0, lds3, lds1, lds4, kt);
+      step_split(lds1, lds4, lds2, lds3, kt + 1);
+      step_split(lds2, lds3, lds0, lds4, kt + 2);
+      step_split(lds0, lds4, lds1, lds3, kt + 3);
+      step_split(lds1, lds3, lds2, lds4, kt + 4);
+      step_split(lds2, lds4, lds0, lds3, kt + 5);
+    }
+  } else {
 #pragma unroll
-  for (int s = 0; s < T::S; ++s) issue(ring[s], s);
-  wait_vmcnt<(T::S - 1) * T::D>();
-  barrier();
-  frag(ring[0], 0, 0);
-  for (int kt = 0; kt < KTr; kt += T::S) {
-    if constexpr (T::S == 2) {
-      step(lds0, lds1, kt);
-      step(lds1, lds0, kt + 1);
-    } else if constexpr (T::S == 3) {
-      step(lds0, lds1, kt);
-      step(lds1, lds2, kt + 1);
-      step(lds2, lds0, kt + 2);
-    } else {
-      step(lds0, lds1, kt);
-      step(lds1, lds2, kt + 1);
-      step(lds2, lds3, kt + 2);
-      step(lds3, lds0, kt + 3);
+    for (int s = 0; s < T::S; ++s) issue(ring[s], s);
+    wait_vmcnt<(T::S - 1) * T::D>();
+    barrier();
+    frag(ring[0], 0, 0);
+    for (int kt = 0; kt < KTr; kt += T::S) {
+      if constexpr (T::S == 2) {
+        step(lds0, lds1, kt);
+        step(lds1, lds0, kt + 1);
+      } else if constexpr (T::S == 3) {
+        step(lds0, lds1, kt);
+        step(lds1, lds2, kt + 1);
+        step(lds2, lds0, kt + 2);
+      } else {
+        step(lds0, lds1, kt);
+        step(lds1, lds2, kt + 1);
+        step(lds2, lds3, kt + 2);
+        step(lds3, lds0, kt + 3);
+      }
     }
   }
   wait_vmcnt<0>();
@@ -291,8 +368,9 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
   if constexpr (EPI == Epilogue::kBf16ScaleBias) {
     // The block's channel scales and bias (as fp32) go to LDS once, so each
     // group of 4 outputs needs two 16-byte LDS reads instead of 8 global loads.
-    float* s_lds = sbias;
-    float* b_lds = sbias + T::BN;
+    float* s_lds = reinterpret_cast<float*>(lds1);   // ring slot 1 is free after the K loop
+    float* b_lds = s_lds + T::BN;
+    static_assert(2 * T::BN * 4 <= T::kSlotBytes, "scales and bias fit in a ring slot");
     static_assert(T::BN <= T::kThreads, "one thread per channel of the block");
     if (tid < T::BN) {
       s_lds[tid] = sw_pre;
@@ -321,7 +399,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
       constexpr int RCH = RB / 16;                    // 16-byte chunks per region row
       constexpr int RWIN = RB >= 256 ? 1 : 256 / RB;  // region rows per 256-byte bank window
       constexpr int RPI = kDmaBytes / RB;             // rows per wavefront store
-      static_assert(T::kWaves * 32 * RB <= T::kStageBytes, "regions fit in one ring slot");
+      static_assert(T::kWaves * 32 * RB <= T::kSlotBytes, "regions fit in one ring slot");
       int8_t* region = lds0 + wave * 32 * RB;
       auto rsw = [](int r, int c) { return c ^ ((r / RWIN) & (RCH - 1)); };
       const int n = n0 + wn * T::TN + (lane % RCH) * 8;   // this lane's 8 channels when storing
@@ -427,11 +505,13 @@ using T2 = Tile<256, 256, 64, 2, 4, 3>;
 using T3 = Tile<256, 128, 128, 2, 2, 3>;
 using T4 = Tile<128, 128, 64, 2, 2, 4>;
 using T5 = Tile<64, 64, 64, 2, 2, 3>;
+using T6 = Tile<256, 256, 128, 2, 4, 0>;
 
 template <class T>
 constexpr TileDesc desc() { return TileDesc{T::BM, T::BN, T::BK, T::kThreads}; }
 
-const TileDesc kTiles[] = {desc<T0>(), desc<T1>(), desc<T2>(), desc<T3>(), desc<T4>(), desc<T5>()};
+const TileDesc kTiles[] = {desc<T0>(), desc<T1>(), desc<T2>(), desc<T3>(), desc<T4>(), desc<T5>(),
+                           desc<T6>()};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
 }  // namespace
@@ -441,16 +521,20 @@ const TileDesc& tile_desc(int tile) { return kTiles[tile]; }
 
 // Shape -> tile, from sweeps of every tile over the DiT shapes on MI355X:
 // 256x256 tiles with 128-byte stages win whenever they give every CU at
-// least one tile; below that, 256x128, then 128x128, then 64x64 tiles keep
-// the 256 CUs busy.
+// least one tile -- the split-ring variant when K is a multiple of 6 stages
+// (or close enough that its zero-padded stages cost < 5%); below that,
+// 256x128, then 128x128, then 64x64 tiles keep the 256 CUs busy.
 int select_tile(int64_t M, int64_t N, int64_t K) {
-  (void)K;
   const int64_t cus = 256;
   auto tiles = [&](int t) {
     return ((M + kTiles[t].block_m - 1) / kTiles[t].block_m) *
            ((N + kTiles[t].block_n - 1) / kTiles[t].block_n);
   };
-  if (tiles(1) >= cus) return 1;
+  if (tiles(1) >= cus) {
+    const int64_t kt = (K + 127) / 128;
+    const int64_t kt6 = (kt + 5) / 6 * 6;
+    return (kt6 - kt) * 20 <= kt ? 6 : 1;
+  }
   if (tiles(3) >= cus / 2) return 3;
   if (tiles(4) >= cus / 2) return 4;
   return 5;
@@ -466,6 +550,7 @@ hipError_t launch_gemm(int tile, Epilogue epi, const int8_t* xq, const int8_t* w
     case 3: return launch_t<T3>(epi, xq, wq, sx, sw, bias, out, M, N, K, stream);
     case 4: return launch_t<T4>(epi, xq, wq, sx, sw, bias, out, M, N, K, stream);
     case 5: return launch_t<T5>(epi, xq, wq, sx, sw, bias, out, M, N, K, stream);
+    case 6: return launch_t<T6>(epi, xq, wq, sx, sw, bias, out, M, N, K, stream);
     default: return hipErrorInvalidValue;
   }
 }
