@@ -122,6 +122,19 @@ def test_ragged_shapes(w, M, N, K):
         run_linear_check(w, x, W, b, tile=tile, label=f"ragged tile{tile}")
 
 
+@pytest.mark.parametrize("M,N,K", [(4096, 4352, 256), (4100, 4344, 272)])
+def test_main_plus_tail_split(w, M, N, K):
+    """Shapes whose 256x256 tiles overflow a whole wave of the 256 CUs by one
+    column: the leading columns run as 256x256 tiles, the rest as a second
+    launch of 128x256 tiles writing into the same output rows."""
+    x = datagen.random_bf16((M, K), seed=M)
+    W = datagen.random_bf16((N, K), seed=N, std=0.02)
+    b = datagen.random_bf16((N,), seed=K, std=0.01)
+    rows = sample_rows(M, 48, 7)
+    for tile in range(w.num_tiles()):
+        run_linear_check(w, x, W, b, rows, tile=tile, label=f"split tile{tile}")
+
+
 def test_special_rows(w):
     """Zero rows give exactly the bias; huge, tiny (subnormal-scale) and
     single-spike rows quantize bit-exactly."""

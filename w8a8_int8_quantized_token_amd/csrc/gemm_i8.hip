@@ -72,16 +72,19 @@ struct Tile {
   static constexpr int DW = BN / kDmaRows / kWaves;  // W DMAs per wavefront per stage
   static constexpr int D = DX + DW;
   static constexpr int kStageBytes = (BM + BN) * BK;
-  static constexpr int kSlotBytes = kSplit ? BM * BK : kStageBytes;   // bytes per LDS array
+  // LDS arrays: split ring -> lds0..2 hold X stages, lds3..4 W stages;
+  // otherwise lds0..S-1 hold whole stages.
   static constexpr int kSlots = kSplit ? 5 : S;
+  static constexpr int kArr012 = kSplit ? BM * BK : kStageBytes;
+  static constexpr int kArr34 = kSplit ? BN * BK : kStageBytes;
+  static constexpr int kLdsBytes = kSplit ? 3 * kArr012 + 2 * kArr34 : S * kStageBytes;
   static_assert(BK == 64 || BK == 128, "64- or 128-byte stages");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(DX >= 1 && DW >= 1 && DX * kDmaRows * kWaves == BM && DW * kDmaRows * kWaves == BN,
                 "every wavefront moves whole DMA blocks of X and W");
   static_assert(S >= 2 && S <= 4, "ring of 2 to 4 stages");
   static_assert((S - 1) * D <= 63, "vmcnt range");
-  static_assert(!kSplit || BM == BN, "split ring slots hold X or W");
-  static_assert(kSlots * kSlotBytes <= 160 * 1024, "LDS budget");
+  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
 // Physical 16-byte chunk of logical chunk c in LDS row r (CPR chunks per
@@ -132,14 +135,14 @@ template <class T, Epilogue EPI>
 __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     const int8_t* __restrict__ X, const int8_t* __restrict__ W, const float* __restrict__ sx,
     const float* __restrict__ sw, const uint16_t* __restrict__ bias, void* __restrict__ out,
-    int M, int N, int K, int tiles_m, int tiles_n, int vec_store) {
+    int M, int N, int K, int ldy, int tiles_m, int tiles_n, int vec_store) {
   // One array per ring slot: distinct objects let the compiler see that a
   // DMA into one slot never aliases fragment reads from another.
-  __shared__ __attribute__((aligned(16))) int8_t lds0[T::kSlotBytes];
-  __shared__ __attribute__((aligned(16))) int8_t lds1[T::kSlotBytes];
-  __shared__ __attribute__((aligned(16))) int8_t lds2[T::kSlots > 2 ? T::kSlotBytes : 16];
-  __shared__ __attribute__((aligned(16))) int8_t lds3[T::kSlots > 3 ? T::kSlotBytes : 16];
-  __shared__ __attribute__((aligned(16))) int8_t lds4[T::kSlots > 4 ? T::kSlotBytes : 16];
+  __shared__ __attribute__((aligned(16))) int8_t lds0[T::kArr012];
+  __shared__ __attribute__((aligned(16))) int8_t lds1[T::kArr012];
+  __shared__ __attribute__((aligned(16))) int8_t lds2[T::kSlots > 2 ? T::kArr012 : 16];
+  __shared__ __attribute__((aligned(16))) int8_t lds3[T::kSlots > 3 ? T::kArr34 : 16];
+  __shared__ __attribute__((aligned(16))) int8_t lds4[T::kSlots > 4 ? T::kArr34 : 16];
   int8_t* const ring[4] = {lds0, lds1, lds2, lds3};
 
   // ---- workgroup -> output tile (XCD-aware, grouped along M) ----
@@ -368,9 +371,19 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
   if constexpr (EPI == Epilogue::kBf16ScaleBias) {
     // The block's channel scales and bias (as fp32) go to LDS once, so each
     // group of 4 outputs needs two 16-byte LDS reads instead of 8 global loads.
-    float* s_lds = reinterpret_cast<float*>(lds1);   // ring slot 1 is free after the K loop
+    // After the K loop the ring is free: the wavefronts' transpose regions
+    // take lds0 (and lds1 if they do not fit), the scales and bias the next
+    // array.
+    constexpr int RB = T::TN * 2;                          // bytes per region row
+    constexpr int kRegion = 32 * RB;                       // 32 rows per wavefront
+    constexpr int kPerArr = T::kArr012 / kRegion;          // regions per array
+    static_assert(kPerArr >= 1 && (T::kWaves + kPerArr - 1) / kPerArr <= 2, "regions fit in lds0/lds1");
+    constexpr bool kOneArr = T::kWaves <= kPerArr;
+    int8_t* const sb_arr = kOneArr ? lds1 : lds2;
+    static_assert(kOneArr || T::kSlots > 2, "a third array holds the scales");
+    float* s_lds = reinterpret_cast<float*>(sb_arr);
     float* b_lds = s_lds + T::BN;
-    static_assert(2 * T::BN * 4 <= T::kSlotBytes, "scales and bias fit in a ring slot");
+    static_assert(2 * T::BN * 4 <= T::kArr012, "scales and bias fit in one array");
     static_assert(T::BN <= T::kThreads, "one thread per channel of the block");
     if (tid < T::BN) {
       s_lds[tid] = sw_pre;
@@ -395,14 +408,17 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
       // results around in its own LDS region and writes whole 16-byte row
       // chunks, so a store instruction covers full 128-byte lines instead of
       // 32 scattered 16-byte pieces.
-      constexpr int RB = T::TN * 2;                   // bytes per region row
       constexpr int RCH = RB / 16;                    // 16-byte chunks per region row
+      constexpr bool kPow2 = (RCH & (RCH - 1)) == 0;
       constexpr int RWIN = RB >= 256 ? 1 : 256 / RB;  // region rows per 256-byte bank window
-      constexpr int RPI = kDmaBytes / RB;             // rows per wavefront store
-      static_assert(T::kWaves * 32 * RB <= T::kSlotBytes, "regions fit in one ring slot");
-      int8_t* region = lds0 + wave * 32 * RB;
-      auto rsw = [](int r, int c) { return c ^ ((r / RWIN) & (RCH - 1)); };
+      constexpr int RPI = kWave / RCH;                // rows per wavefront store
+      constexpr int NIT = (32 + RPI - 1) / RPI;       // stores per 32 rows
+      int8_t* region = (wave < kPerArr ? lds0 + wave * kRegion : lds1 + (wave - kPerArr) * kRegion);
+      // XOR swizzle of the 16-byte chunks for power-of-two row widths (the
+      // 96-channel rows of 192-wide tiles are read linearly instead)
+      auto rsw = [](int r, int c) { return kPow2 ? (c ^ ((r / RWIN) & (RCH - 1))) : c; };
       const int n = n0 + wn * T::TN + (lane % RCH) * 8;   // this lane's 8 channels when storing
+      const bool lane_on = lane < RPI * RCH;
 #pragma unroll
       for (int i = 0; i < T::FM; ++i) {
         const int mb = m0 + wm * T::TM + i * 32;
@@ -416,17 +432,18 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
                 u32x2{wlo, whi};
           }
         }
-        v4i v[32 / RPI];
+        v4i v[NIT];
 #pragma unroll
-        for (int it = 0; it < 32 / RPI; ++it) {
-          const int r = it * RPI + lane / RCH;
+        for (int it = 0; it < NIT; ++it) {
+          const int r = min(it * RPI + lane / RCH, 31);
           v[it] = *reinterpret_cast<const v4i*>(region + r * RB + rsw(r, lane % RCH) * 16);
         }
 #pragma unroll
-        for (int it = 0; it < 32 / RPI; ++it) {
-          const int m = mb + it * RPI + lane / RCH;
-          if (m < M && n < N)
-            *reinterpret_cast<v4i*>(reinterpret_cast<uint16_t*>(out) + (int64_t)m * N + n) = v[it];
+        for (int it = 0; it < NIT; ++it) {
+          const int r = it * RPI + lane / RCH;
+          const int m = mb + r;
+          if (lane_on && r < 32 && m < M && n < N)
+            *reinterpret_cast<v4i*>(reinterpret_cast<uint16_t*>(out) + (int64_t)m * ldy + n) = v[it];
         }
       }
     } else {
@@ -434,7 +451,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
       for (int i = 0; i < T::FM; ++i) {
         const int m = m0 + wm * T::TM + i * 32 + row_in;
         if (m >= M) continue;
-        uint16_t* yrow = reinterpret_cast<uint16_t*>(out) + (int64_t)m * N;
+        uint16_t* yrow = reinterpret_cast<uint16_t*>(out) + (int64_t)m * ldy;
         const float sa = sa_pre[i];
 #pragma unroll
         for (int j = 0; j < T::FN; ++j) {
@@ -457,7 +474,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     for (int i = 0; i < T::FM; ++i) {
       const int m = m0 + wm * T::TM + i * 32 + row_in;
       if (m >= M) continue;
-      int32_t* crow = reinterpret_cast<int32_t*>(out) + (int64_t)m * N;
+      int32_t* crow = reinterpret_cast<int32_t*>(out) + (int64_t)m * ldy;
 #pragma unroll
       for (int j = 0; j < T::FN; ++j) {
 #pragma unroll
@@ -477,82 +494,135 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
   }
 }
 
+// Launch tile configuration T on the sub-problem M x N x K whose output rows
+// are `ldy` elements apart.
 template <class T>
 hipError_t launch_t(Epilogue epi, const int8_t* xq, const int8_t* wq, const float* sx,
                     const float* sw, const uint16_t* bias, void* out, int64_t M, int64_t N,
-                    int64_t K, hipStream_t stream) {
+                    int64_t K, int64_t ldy, hipStream_t stream) {
   const int tiles_m = (int)((M + T::BM - 1) / T::BM);
   const int tiles_n = (int)((N + T::BN - 1) / T::BN);
   const dim3 grid((unsigned)(tiles_m * tiles_n));
   const dim3 block(T::kThreads);
   const uintptr_t o = reinterpret_cast<uintptr_t>(out);
   if (epi == Epilogue::kBf16ScaleBias) {
-    const int vec = (N % 8 == 0) && (o % 16 == 0);
+    const int vec = (ldy % 8 == 0) && (o % 16 == 0);
     hipLaunchKernelGGL((gemm_i8_kernel<T, Epilogue::kBf16ScaleBias>), grid, block, 0, stream, xq,
-                       wq, sx, sw, bias, out, (int)M, (int)N, (int)K, tiles_m, tiles_n, vec);
-  } else {
-    const int vec = (N % 4 == 0) && (o % 16 == 0);
-    hipLaunchKernelGGL((gemm_i8_kernel<T, Epilogue::kRawI32>), grid, block, 0, stream, xq, wq,
-                       nullptr, nullptr, nullptr, out, (int)M, (int)N, (int)K, tiles_m, tiles_n,
+                       wq, sx, sw, bias, out, (int)M, (int)N, (int)K, (int)ldy, tiles_m, tiles_n,
                        vec);
+  } else {
+    const int vec = (ldy % 4 == 0) && (o % 16 == 0);
+    hipLaunchKernelGGL((gemm_i8_kernel<T, Epilogue::kRawI32>), grid, block, 0, stream, xq, wq,
+                       nullptr, nullptr, nullptr, out, (int)M, (int)N, (int)K, (int)ldy, tiles_m,
+                       tiles_n, vec);
   }
   return hipGetLastError();
 }
 
-using T0 = Tile<256, 256, 64, 2, 4, 4>;
-using T1 = Tile<256, 256, 128, 2, 4, 2>;
-using T2 = Tile<256, 256, 64, 2, 4, 3>;
-using T3 = Tile<256, 128, 128, 2, 2, 3>;
-using T4 = Tile<128, 128, 64, 2, 2, 4>;
-using T5 = Tile<64, 64, 64, 2, 2, 3>;
-using T6 = Tile<256, 256, 128, 2, 4, 0>;
+// Compiled tile configurations.
+using CfgSplit = Tile<256, 256, 128, 2, 4, 0>;   // 256x256, X two stages ahead, W one
+using CfgWhole = Tile<256, 256, 128, 2, 4, 2>;   // 256x256, two whole stages
+using Cfg192 = Tile<256, 192, 128, 4, 2, 0>;     // 256x192, split ring
+using CfgTail = Tile<128, 256, 128, 2, 4, 3>;    // 128x256, three whole stages
+using Cfg256x128 = Tile<256, 128, 128, 2, 2, 3>;
+using Cfg128 = Tile<128, 128, 64, 2, 2, 4>;
+using Cfg64 = Tile<64, 64, 64, 2, 2, 3>;
 
 template <class T>
 constexpr TileDesc desc() { return TileDesc{T::BM, T::BN, T::BK, T::kThreads}; }
 
-const TileDesc kTiles[] = {desc<T0>(), desc<T1>(), desc<T2>(), desc<T3>(), desc<T4>(), desc<T5>(),
-                           desc<T6>()};
-constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+enum Cfg { kSplit256, kWhole256, k192, kTail128x256, k256x128, k128, k64, kNumCfg };
+const TileDesc kCfgs[kNumCfg] = {desc<CfgSplit>(), desc<CfgWhole>(), desc<Cfg192>(),
+                                 desc<CfgTail>(), desc<Cfg256x128>(), desc<Cfg128>(),
+                                 desc<Cfg64>()};
+
+hipError_t launch_cfg(int cfg, Epilogue epi, const int8_t* xq, const int8_t* wq, const float* sx,
+                      const float* sw, const uint16_t* bias, void* out, int64_t M, int64_t N,
+                      int64_t K, int64_t ldy, hipStream_t s) {
+  switch (cfg) {
+    case kSplit256: return launch_t<CfgSplit>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
+    case kWhole256: return launch_t<CfgWhole>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
+    case k192: return launch_t<Cfg192>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
+    case kTail128x256: return launch_t<CfgTail>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
+    case k256x128: return launch_t<Cfg256x128>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
+    case k128: return launch_t<Cfg128>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
+    case k64: return launch_t<Cfg64>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// A plan ("tile id" of the C ABI) is a main configuration, optionally with
+// a tail: when the main tiles do not come out as whole waves of 256
+// workgroups (one per CU), the leading output-channel columns that do are
+// done with the main tiles and the remaining columns with 128x256 tiles in a
+// second launch, so the last wave of big tiles does not run on a
+// half-empty GPU.
+struct Plan {
+  int main;
+  int tail;   // -1: none
+};
+constexpr Plan kPlans[] = {
+    {kSplit256, kTail128x256}, {kSplit256, -1}, {kWhole256, kTail128x256}, {kWhole256, -1},
+    {k192, -1}, {kTail128x256, -1}, {k256x128, -1}, {k128, -1}, {k64, -1}};
+constexpr int kNumPlans = sizeof(kPlans) / sizeof(kPlans[0]);
+constexpr int kCUs = 256;
+
+// Leading columns of main tiles that form whole waves (0: no useful split).
+int64_t main_columns(const TileDesc& d, int64_t M, int64_t N) {
+  const int64_t tm = (M + d.block_m - 1) / d.block_m, tn = (N + d.block_n - 1) / d.block_n;
+  if ((tm * tn) % kCUs == 0) return 0;
+  const int64_t rounds = (tm * tn + kCUs - 1) / kCUs;
+  const TileDesc& t = kCfgs[kTail128x256];
+  for (int64_t c = tn - 1; c >= 1; --c) {
+    if ((tm * c) % kCUs != 0) continue;
+    const int64_t tail = ((M + t.block_m - 1) / t.block_m) *
+                         ((N - c * d.block_n + t.block_n - 1) / t.block_n);
+    // a tail wave of half-height tiles costs about 0.6 of a wave of main tiles
+    const double est = (double)(tm * c / kCUs) + 0.6 * (double)((tail + kCUs - 1) / kCUs);
+    return est + 0.1 < (double)rounds ? c : 0;
+  }
+  return 0;
+}
 
 }  // namespace
 
-int num_tiles() { return kNumTiles; }
-const TileDesc& tile_desc(int tile) { return kTiles[tile]; }
+int num_tiles() { return kNumPlans; }
+const TileDesc& tile_desc(int tile) { return kCfgs[kPlans[tile].main]; }
 
-// Shape -> tile, from sweeps of every tile over the DiT shapes on MI355X:
-// 256x256 tiles with 128-byte stages win whenever they give every CU at
-// least one tile -- the split-ring variant when K is a multiple of 6 stages
-// (or close enough that its zero-padded stages cost < 5%); below that,
-// 256x128, then 128x128, then 64x64 tiles keep the 256 CUs busy.
+// Shape -> plan, from sweeps over the DiT shapes on MI355X: 256x256 tiles with
+// 128-byte stages (plus the 128x256 tail) whenever they give every CU at least
+// one tile -- the split ring when K is a multiple of 6 stages or close enough
+// that its zero-padded stages cost < 5%; below that, 256x128, then 128x128,
+// then 64x64 tiles keep the 256 CUs busy.
 int select_tile(int64_t M, int64_t N, int64_t K) {
-  const int64_t cus = 256;
-  auto tiles = [&](int t) {
-    return ((M + kTiles[t].block_m - 1) / kTiles[t].block_m) *
-           ((N + kTiles[t].block_n - 1) / kTiles[t].block_n);
+  auto tiles = [&](int cfg) {
+    return ((M + kCfgs[cfg].block_m - 1) / kCfgs[cfg].block_m) *
+           ((N + kCfgs[cfg].block_n - 1) / kCfgs[cfg].block_n);
   };
-  if (tiles(1) >= cus) {
+  if (tiles(kSplit256) >= kCUs) {
     const int64_t kt = (K + 127) / 128;
     const int64_t kt6 = (kt + 5) / 6 * 6;
-    return (kt6 - kt) * 20 <= kt ? 6 : 1;
+    return (kt6 - kt) * 20 <= kt ? 0 : 2;
   }
-  if (tiles(3) >= cus / 2) return 3;
-  if (tiles(4) >= cus / 2) return 4;
-  return 5;
+  if (tiles(k256x128) >= kCUs / 2) return 6;
+  if (tiles(k128) >= kCUs / 2) return 7;
+  return 8;
 }
 
 hipError_t launch_gemm(int tile, Epilogue epi, const int8_t* xq, const int8_t* wq,
                        const float* sx, const float* sw, const uint16_t* bias, void* out,
                        int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  switch (tile) {
-    case 0: return launch_t<T0>(epi, xq, wq, sx, sw, bias, out, M, N, K, stream);
-    case 1: return launch_t<T1>(epi, xq, wq, sx, sw, bias, out, M, N, K, stream);
-    case 2: return launch_t<T2>(epi, xq, wq, sx, sw, bias, out, M, N, K, stream);
-    case 3: return launch_t<T3>(epi, xq, wq, sx, sw, bias, out, M, N, K, stream);
-    case 4: return launch_t<T4>(epi, xq, wq, sx, sw, bias, out, M, N, K, stream);
-    case 5: return launch_t<T5>(epi, xq, wq, sx, sw, bias, out, M, N, K, stream);
-    case 6: return launch_t<T6>(epi, xq, wq, sx, sw, bias, out, M, N, K, stream);
-    default: return hipErrorInvalidValue;
-  }
+  if (tile < 0 || tile >= kNumPlans) return hipErrorInvalidValue;
+  const Plan& p = kPlans[tile];
+  const int64_t c = p.tail >= 0 ? main_columns(kCfgs[p.main], M, N) : 0;
+  if (c == 0) return launch_cfg(p.main, epi, xq, wq, sx, sw, bias, out, M, N, K, N, stream);
+  const int64_t nm = c * kCfgs[p.main].block_n;   // channels done by the main tiles
+  hipError_t e = launch_cfg(p.main, epi, xq, wq, sx, sw, bias, out, M, nm, K, N, stream);
+  if (e != hipSuccess) return e;
+  const size_t esz = epi == Epilogue::kBf16ScaleBias ? 2 : 4;
+  void* out_tail = static_cast<char*>(out) + nm * esz;
+  return launch_cfg(p.tail, epi, xq, wq + nm * K, sx, sw ? sw + nm : nullptr,
+                    bias ? bias + nm : nullptr, out_tail, M, N - nm, K, N, stream);
 }
 
 }  // namespace w8a8
