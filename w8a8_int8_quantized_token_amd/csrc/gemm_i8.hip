@@ -9,27 +9,35 @@
 // v_mfma_i32_32x32x32_i8 (each lane supplies 16 consecutive K bytes of one
 // row).  The MFMA's first operand takes W rows and its second X rows, so the
 // 32x32 result a lane holds is one token (column) by 16 output channels in
-// four runs of 4 consecutive channels: the epilogue writes 8-byte runs of a
-// row of Y without any transpose.
+// four runs of 4 consecutive channels, i.e. 8-byte runs of a row of Y; the
+// epilogue passes each 32x32 tile through LDS so that a store instruction
+// writes 64-byte row pieces.
 //
 // Pipeline: a workgroup owns a BM x BN output tile and walks K in stages of
-// 64 bytes.  Stages go straight from global memory into a ring of S LDS
-// buffers with buffer_load ... lds (no staging registers, no LDS store
-// instructions); a stage is requested S-1 stages before it is used.  Chunks
-// past K or rows past M/N are requested at an out-of-range buffer offset,
-// which the hardware returns as zeros, so partial tiles need no branches and
-// stages past the end add nothing.  Fragments are read with 16-byte LDS
-// reads, one MFMA K step ahead of the MFMAs that use them, including across
-// the stage boundary.  16-byte chunks are XOR swizzled within each LDS row so
-// that neither the DMA writes nor the fragment reads conflict on banks.  The
-// accumulators stay in registers for the whole K loop; int32 never touches
-// HBM on the fused path.
+// BK bytes (128 for the large tiles).  Stages go straight from global memory
+// into LDS with buffer_load ... lds (no staging registers, no LDS store
+// instructions).  The large tiles use a split ring: three X slots and two W
+// slots, so X is requested two stages ahead and W one; the other tiles use a
+// ring of S whole stages.  Chunks past K or rows past M/N are requested at
+// an out-of-range buffer offset, which the hardware returns as zeros, so
+// partial tiles need no branches and stages past the end add nothing.
+// Fragments are read with 16-byte LDS reads, one MFMA K step ahead of the
+// MFMAs that use them, including across the stage boundary.  16-byte chunks
+// are XOR swizzled within each LDS row so that neither the DMA writes nor
+// the fragment reads conflict on banks.  The accumulators stay in registers
+// for the whole K loop; int32 never touches HBM on the fused path.
+//
+// Persistence: one workgroup per CU walks its share of the tiles; with the
+// split ring the first stage of its next tile is requested before the
+// epilogue of the current one.
 //
 // Workgroup order: consecutive workgroup ids are dispatched round robin over
-// the 8 XCDs, each with its own L2.  Ids are remapped so that each XCD gets a
-// contiguous range of tiles, and that range is walked in groups of kGroupM
-// tile rows, so the tiles resident on one XCD share X and W panels in its L2.
+// the 8 XCDs, each with its own L2.  Tiles are remapped so that each XCD gets
+// a contiguous range, walked in groups of kGroupM tile rows, so the tiles
+// resident on one XCD share X and W panels in its L2.
 #include "kernels.h"
+
+#include <algorithm>
 
 namespace w8a8 {
 namespace {
@@ -131,6 +139,28 @@ __device__ __forceinline__ void barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Output tile `t` (0 <= t < tiles_m * tiles_n) -> (first row, first channel).
+// Tiles are spread so that each XCD works on a contiguous range, walked in
+// groups of kGroupM tile rows (tiles resident on one XCD share X and W panels
+// in its L2).  A workgroup on XCD x only ever gets tiles of XCD x's range:
+// grid sizes are multiples of 8 whenever tile counts are.
+__device__ __forceinline__ void tile_origin(int t, int tiles_m, int tiles_n, int bm, int bn,
+                                            int& m0, int& n0) {
+  const int ntiles = tiles_m * tiles_n;
+  if (ntiles % kNumXcd == 0) t = (t % kNumXcd) * (ntiles / kNumXcd) + t / kNumXcd;
+  const int per_group = kGroupM * tiles_n;
+  const int group = t / per_group;
+  const int first_m = group * kGroupM;
+  const int gsize = min(tiles_m - first_m, kGroupM);
+  const int in_group = t - group * per_group;
+  m0 = (first_m + in_group % gsize) * bm;
+  n0 = (in_group / gsize) * bn;
+}
+
+// Persistent kernel: gridDim.x workgroups (at most one per CU) walk the
+// output tiles t = blockIdx.x, blockIdx.x + gridDim.x, ...  With the split
+// ring, the first two requests of a workgroup's next tile are issued before
+// the epilogue of the current one, so the epilogue hides their latency.
 template <class T, Epilogue EPI>
 __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     const int8_t* __restrict__ X, const int8_t* __restrict__ W, const float* __restrict__ sx,
@@ -145,105 +175,83 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
   __shared__ __attribute__((aligned(16))) int8_t lds4[T::kSlots > 4 ? T::kArr34 : 16];
   int8_t* const ring[4] = {lds0, lds1, lds2, lds3};
 
-  // ---- workgroup -> output tile (XCD-aware, grouped along M) ----
   const int ntiles = tiles_m * tiles_n;
-  int bid = blockIdx.x;
-  if (ntiles % kNumXcd == 0) bid = (bid % kNumXcd) * (ntiles / kNumXcd) + bid / kNumXcd;
-  const int per_group = kGroupM * tiles_n;
-  const int group = bid / per_group;
-  const int first_m = group * kGroupM;
-  const int gsize = min(tiles_m - first_m, kGroupM);
-  const int in_group = bid - group * per_group;
-  const int tm = first_m + in_group % gsize;
-  const int tn = in_group / gsize;
-  const int m0 = tm * T::BM, n0 = tn * T::BN;
-
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / T::WN, wn = wave % T::WN;
+  const int row_in = lane % 32;   // row of the 32-row MFMA operand this lane feeds
+  const int khalf = lane / 32;    // which 16-byte half of each 32-byte K step
+  const int KT = (K + T::BK - 1) / T::BK;
 
   // ---- DMA addressing ----
   // Lane p of a DMA fills LDS slot p of a block of kDmaRows rows (DMA writes
   // are linear, hence conflict-free): row r = block*kDmaRows + p/CPR,
   // physical chunk p%CPR, so the lane fetches logical chunk swz(r, p%CPR).
-  const int rows_x = min(T::BM, M - m0), rows_w = min(T::BN, N - n0);
-  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int8_t*>(X + (int64_t)m0 * K), (short)0, rows_x * K, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int8_t*>(W + (int64_t)n0 * K), (short)0, rows_w * K, kRsrcWord3);
-  const int dma_r = lane / T::CPR;
-  int xcol[T::DX], wcol[T::DW];        // K byte offset of the lane's chunk in a stage
-  uint32_t xrow[T::DX], wrow[T::DW];   // byte offset of that chunk in stage 0, or kOOB
-#pragma unroll
-  for (int i = 0; i < T::DX; ++i) {
-    const int r = (wave + i * T::kWaves) * T::kDmaRows + dma_r;
-    xcol[i] = swz<T::CPR>(r, lane % T::CPR) * 16;
-    xrow[i] = r < rows_x ? (uint32_t)(r * K + xcol[i]) : kOOB;
-  }
-#pragma unroll
-  for (int i = 0; i < T::DW; ++i) {
-    const int r = (wave + i * T::kWaves) * T::kDmaRows + dma_r;
-    wcol[i] = swz<T::CPR>(r, lane % T::CPR) * 16;
-    wrow[i] = r < rows_w ? (uint32_t)(r * K + wcol[i]) : kOOB;
-  }
-  // Request the X (W) part of stage kt into `buf`; chunks at or past K read
-  // as zeros.
-  auto issue_x = [&](int8_t* buf, int kt) {
+  // Wavefront w moves blocks w, w + kWaves, ... of X and of W; the swizzle
+  // repeats every 16 rows, so the chunk a lane fetches is the same in all of
+  // them.  Its byte offset in stage 0 of a tile is the same for every tile:
+  // rows past M (N) fall outside the tile's buffer resource, whose range
+  // ends with the tile's last valid row, and read as zeros.
+  static_assert((T::kWaves * T::kDmaRows) % 16 == 0, "one swizzle phase per DMA block set");
+  const int dma_r = wave * T::kDmaRows + lane / T::CPR;
+  const int col = swz<T::CPR>(dma_r, lane % T::CPR) * 16;   // K byte offset within a stage
+  const uint32_t off0 = (uint32_t)(dma_r * K + col);
+  const uint32_t blk_stride = (uint32_t)(T::kWaves * T::kDmaRows * K);
+
+  // Per-tile state (wavefront-uniform): origin and buffer resources over the
+  // tile's rows of X and W.
+  struct TileAddr {
+    int m0, n0;
+    __amdgpu_buffer_rsrc_t rx, rw;
+  };
+  auto setup = [&](int t, TileAddr& a) {
+    tile_origin(t, tiles_m, tiles_n, T::BM, T::BN, a.m0, a.n0);
+    const int rows_x = min(T::BM, M - a.m0), rows_w = min(T::BN, N - a.n0);
+    a.rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(X + (int64_t)a.m0 * K), (short)0,
+                                             rows_x * K, kRsrcWord3);
+    a.rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(W + (int64_t)a.n0 * K), (short)0,
+                                             rows_w * K, kRsrcWord3);
+  };
+  // Request the X (W) part of stage kt of tile `a` into `buf`; chunks at or
+  // past K read as zeros.
+  auto issue_x = [&](const TileAddr& a, int8_t* buf, int kt) {
     const int kb = kt * T::BK;
+    const bool in_k = kb + col < K;
 #pragma unroll
     for (int i = 0; i < T::DX; ++i)
-      dma16(rx, buf + (wave + i * T::kWaves) * kDmaBytes,
-            kb + xcol[i] < K ? xrow[i] + (uint32_t)kb : kOOB);
+      dma16(a.rx, buf + (wave + i * T::kWaves) * kDmaBytes,
+            in_k ? off0 + (uint32_t)(i * blk_stride + kb) : kOOB);
   };
-  auto issue_w = [&](int8_t* buf, int kt) {
+  auto issue_w = [&](const TileAddr& a, int8_t* buf, int kt) {
     const int kb = kt * T::BK;
+    const bool in_k = kb + col < K;
 #pragma unroll
     for (int i = 0; i < T::DW; ++i)
-      dma16(rw, buf + (wave + i * T::kWaves) * kDmaBytes,
-            kb + wcol[i] < K ? wrow[i] + (uint32_t)kb : kOOB);
+      dma16(a.rw, buf + (wave + i * T::kWaves) * kDmaBytes,
+            in_k ? off0 + (uint32_t)(i * blk_stride + kb) : kOOB);
   };
   // Whole stage kt into ring slot `buf` (X rows first, then W rows).
-  auto issue = [&](int8_t* buf, int kt) {
-    issue_x(buf, kt);
-    issue_w(buf + T::BM * T::BK, kt);
+  auto issue = [&](const TileAddr& a, int8_t* buf, int kt) {
+    issue_x(a, buf, kt);
+    issue_w(a, buf + T::BM * T::BK, kt);
   };
 
   v16i acc[T::FM][T::FN];
-#pragma unroll
-  for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < T::FN; ++j) acc[i][j] = v16i{};
-
-  const int row_in = lane % 32;   // row of the 32-row MFMA operand this lane feeds
-  const int khalf = lane / 32;    // which 16-byte half of each 32-byte K step
-
-  // The epilogue's scales and bias are requested now, ahead of the stage
-  // DMAs, so their latency is hidden by the K loop (the in-order vector memory
-  // counter keeps the DMA waits below exact).
-  float sa_pre[T::FM], sw_pre = 0.0f, b_pre = 0.0f;
-  if constexpr (EPI == Epilogue::kBf16ScaleBias) {
-#pragma unroll
-    for (int i = 0; i < T::FM; ++i) sa_pre[i] = sx[min(m0 + wm * T::TM + i * 32 + row_in, M - 1)];
-    if (tid < T::BN && n0 + tid < N) {
-      sw_pre = sw[n0 + tid];
-      if (bias != nullptr) b_pre = bf16_to_float(bias[n0 + tid]);
-    }
-  }
 
   // Fragment registers, double buffered by MFMA K step parity.
-  v4i a[2][T::FN], b[2][T::FM];
+  v4i fa[2][T::FN], fb[2][T::FM];
   auto frag2 = [&](const int8_t* xs, const int8_t* ws, int s, int slot) {
     const int c = s * 2 + khalf;
 #pragma unroll
     for (int j = 0; j < T::FN; ++j) {
       const int r = wn * T::TN + j * 32 + row_in;
-      a[slot][j] = *reinterpret_cast<const v4i*>(ws + r * T::BK + swz<T::CPR>(r, c) * 16);
+      fa[slot][j] = *reinterpret_cast<const v4i*>(ws + r * T::BK + swz<T::CPR>(r, c) * 16);
     }
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
       const int r = wm * T::TM + i * 32 + row_in;
-      b[slot][i] = *reinterpret_cast<const v4i*>(xs + r * T::BK + swz<T::CPR>(r, c) * 16);
+      fb[slot][i] = *reinterpret_cast<const v4i*>(xs + r * T::BK + swz<T::CPR>(r, c) * 16);
     }
   };
   auto frag = [&](const int8_t* buf, int s, int slot) { frag2(buf, buf + T::BM * T::BK, s, slot); };
@@ -252,7 +260,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     for (int i = 0; i < T::FM; ++i)
 #pragma unroll
       for (int j = 0; j < T::FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[slot][j], b[slot][i], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[slot][j], fb[slot][i], acc[i][j], 0, 0, 0);
   };
 
   // Scheduling of the code after a barrier: the next stage's first fragment
@@ -269,15 +277,12 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  const int KT = (K + T::BK - 1) / T::BK;
-  const int KTr = (KT + T::S - 1) / T::S * T::S;   // stages computed (the extra ones are zeros)
-
   // Step k (stage k in slot `cur`, fragments of its first K step in flight):
   // run the K steps; once every wavefront is past its reads of `cur` and
   // stage k+1 has landed (one barrier), request stage k+S into `cur` and
   // start reading stage k+1's first fragments under the MFMAs of the last K
   // step.  A stage is thus requested a full S-1 steps before it is needed.
-  auto step = [&](int8_t* cur, int8_t* nxt, int k) {
+  auto step = [&](const TileAddr& a, int8_t* cur, int8_t* nxt, int k) {
 #pragma unroll
     for (int s = 0; s + 1 < T::KSUB; ++s) {
       frag(cur, s + 1, (s + 1) & 1);
@@ -289,7 +294,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     wait_vmcnt<(T::S - 2) * T::D>();  // its DMAs of stage k+1 have landed
     barrier();                       // ... and everyone's
     frag(nxt, 0, T::KSUB & 1);
-    issue(cur, k + T::S);
+    issue(a, cur, k + T::S);
     mfmas((T::KSUB - 1) & 1);
     interleave();
   };
@@ -299,7 +304,8 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
   // X_{k+3} are requested into them: at the next barrier only the W part
   // (half a stage, requested one step earlier) is on the critical path, while
   // X has two steps to land.
-  auto step_split = [&](int8_t* xc, int8_t* wc, int8_t* xn, int8_t* wn1, int k) {
+  auto step_split = [&](const TileAddr& a, int8_t* xc, int8_t* wc, int8_t* xn, int8_t* wn1,
+                        int k) {
 #pragma unroll
     for (int s = 0; s + 1 < T::KSUB; ++s) {
       frag2(xc, wc, s + 1, (s + 1) & 1);
@@ -310,188 +316,278 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     wait_lgkmcnt0();
     wait_vmcnt<T::DX>();   // everything but X_{k+2} (the last request) has landed
     barrier();
-    // After the barrier: the next stage's first fragment reads, the last K
-    // step's MFMAs and the next requests, interleaved so that the MFMA pipe
-    // restarts right away instead of waiting for the DMA issue.
     frag2(xn, wn1, 0, T::KSUB & 1);
-    issue_w(wc, k + 2);
-    issue_x(xc, k + 3);
+    issue_w(a, wc, k + 2);
+    issue_x(a, xc, k + 3);
     mfmas((T::KSUB - 1) & 1);
     interleave();
   };
 
-  // ---- main loop over a ring of S slots ----
+  // ---- epilogue placement in LDS (the ring is free after a tile's K loop) ----
+  // Split ring: the transpose regions start at lds1 and the scales/bias come
+  // after them, leaving lds0 and lds3 to the next tile's first requests.
+  // Otherwise the regions start at lds0.
+  constexpr int kRegion = 32 * 64;   // per wavefront: 32 rows x 32 bf16 channels
+  constexpr bool kSbAfter = T::kWaves * kRegion + 2 * T::BN * 4 <= T::kArr012;
+  static_assert(T::kWaves * kRegion <= T::kArr012, "regions fit in one array");
+  static_assert(kSbAfter || (!T::kSplit && 2 * T::BN * 4 <= T::kArr012), "scales and bias fit");
+  int8_t* const reg_a = T::kSplit ? lds1 : lds0;
+  // channel scales and biases (fp32) follow the regions, else take the next array
+  int8_t* const sb_arr = kSbAfter ? reg_a + T::kWaves * kRegion : lds1;
+
+  // Dequant scalars of a tile, requested one tile ahead so that their
+  // latency hides under a K loop: per-token scales of the rows this lane
+  // holds, and (threads below BN) one channel's scale and bias.
+  float sa_n[T::FM], sw_n = 0.0f, b_n = 0.0f;
+  auto load_scalars = [&](const TileAddr& a) {
+    if constexpr (EPI == Epilogue::kBf16ScaleBias) {
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i) sa_n[i] = sx[min(a.m0 + wm * T::TM + i * 32 + row_in, M - 1)];
+      static_assert(T::BN <= T::kThreads, "one thread per channel of the block");
+      sw_n = 0.0f;
+      b_n = 0.0f;
+      if (tid < T::BN && a.n0 + tid < N) {
+        sw_n = sw[a.n0 + tid];
+        if (bias != nullptr) b_n = bf16_to_float(bias[a.n0 + tid]);
+      }
+    }
+  };
+
+  TileAddr cur;
+  setup(blockIdx.x, cur);
+  load_scalars(cur);
   if constexpr (T::kSplit) {
     // X slots lds0..lds2 (X_k in slot k%3), W slots lds3, lds4 (W_k in k%2);
     // the slot pattern repeats every 6 stages.
-    issue_x(lds0, 0);
-    issue_w(lds3, 0);
-    issue_x(lds1, 1);
-    issue_w(lds4, 1);
-    issue_x(lds2, 2);
+    issue_x(cur, lds0, 0);
+    issue_w(cur, lds3, 0);
+    issue_x(cur, lds1, 1);
+    issue_w(cur, lds4, 1);
+    issue_x(cur, lds2, 2);
     wait_vmcnt<2 * T::DX + T::DW>();
     barrier();
     frag2(lds0, lds3, 0, 0);
-    const int KT6 = (KT + 5) / 6 * 6;
-    for (int kt = 0; kt < KT6; kt += 6) {
-      step_split(lds0, lds3, lds1, lds4, kt);
-      step_split(lds1, lds4, lds2, lds3, kt + 1);
-      step_split(lds2, lds3, lds0, lds4, kt + 2);
-      step_split(lds0, lds4, lds1, lds3, kt + 3);
-      step_split(lds1, lds3, lds2, lds4, kt + 4);
-      step_split(lds2, lds4, lds0, lds3, kt + 5);
-    }
-  } else {
-#pragma unroll
-    for (int s = 0; s < T::S; ++s) issue(ring[s], s);
-    wait_vmcnt<(T::S - 1) * T::D>();
-    barrier();
-    frag(ring[0], 0, 0);
-    for (int kt = 0; kt < KTr; kt += T::S) {
-      if constexpr (T::S == 2) {
-        step(lds0, lds1, kt);
-        step(lds1, lds0, kt + 1);
-      } else if constexpr (T::S == 3) {
-        step(lds0, lds1, kt);
-        step(lds1, lds2, kt + 1);
-        step(lds2, lds0, kt + 2);
-      } else {
-        step(lds0, lds1, kt);
-        step(lds1, lds2, kt + 1);
-        step(lds2, lds3, kt + 2);
-        step(lds3, lds0, kt + 3);
-      }
-    }
   }
-  wait_vmcnt<0>();
-  wait_lgkmcnt0();
-  barrier();   // every DMA and fragment read is done before LDS is reused
 
-  // ---- epilogue: lane holds token m, channels n = base + 8*g + 4*khalf + 0..3 ----
-  if constexpr (EPI == Epilogue::kBf16ScaleBias) {
-    // The block's channel scales and bias (as fp32) go to LDS once, so each
-    // group of 4 outputs needs two 16-byte LDS reads instead of 8 global loads.
-    // After the K loop the ring is free: the wavefronts' transpose regions
-    // take lds0 (and lds1 if they do not fit), the scales and bias the next
-    // array.
-    constexpr int RB = T::TN * 2;                          // bytes per region row
-    constexpr int kRegion = 32 * RB;                       // 32 rows per wavefront
-    constexpr int kPerArr = T::kArr012 / kRegion;          // regions per array
-    static_assert(kPerArr >= 1 && (T::kWaves + kPerArr - 1) / kPerArr <= 2, "regions fit in lds0/lds1");
-    constexpr bool kOneArr = T::kWaves <= kPerArr;
-    int8_t* const sb_arr = kOneArr ? lds1 : lds2;
-    static_assert(kOneArr || T::kSlots > 2, "a third array holds the scales");
-    float* s_lds = reinterpret_cast<float*>(sb_arr);
-    float* b_lds = s_lds + T::BN;
-    static_assert(2 * T::BN * 4 <= T::kArr012, "scales and bias fit in one array");
-    static_assert(T::BN <= T::kThreads, "one thread per channel of the block");
-    if (tid < T::BN) {
-      s_lds[tid] = sw_pre;
-      b_lds[tid] = b_pre;
-    }
-    __syncthreads();
-    // 4 bf16 outputs (two packed words) of MFMA tile (i, j), run g.
-    auto outputs = [&](int i, int j, int g, float sa, uint32_t& wlo, uint32_t& whi) {
-      const int nl = wn * T::TN + j * 32 + g * 8 + khalf * 4;
-      const f32x4 sv = *reinterpret_cast<const f32x4*>(s_lds + nl);
-      const f32x4 bv = *reinterpret_cast<const f32x4*>(b_lds + nl);
-      const v16i& c = acc[i][j];
-      const bf16x2 lo = __builtin_convertvector(
-          (f32x2{dequant(c[g * 4], sa, sv[0], bv[0]), dequant(c[g * 4 + 1], sa, sv[1], bv[1])}), bf16x2);
-      const bf16x2 hi = __builtin_convertvector(
-          (f32x2{dequant(c[g * 4 + 2], sa, sv[2], bv[2]), dequant(c[g * 4 + 3], sa, sv[3], bv[3])}), bf16x2);
-      wlo = __builtin_bit_cast(uint32_t, lo);
-      whi = __builtin_bit_cast(uint32_t, hi);
-    };
-    if (vec_store) {
-      // Row-major Y with N % 8 == 0: each wavefront turns 32 rows x TN of its
-      // results around in its own LDS region and writes whole 16-byte row
-      // chunks, so a store instruction covers full 128-byte lines instead of
-      // 32 scattered 16-byte pieces.
-      constexpr int RCH = RB / 16;                    // 16-byte chunks per region row
-      constexpr bool kPow2 = (RCH & (RCH - 1)) == 0;
-      constexpr int RWIN = RB >= 256 ? 1 : 256 / RB;  // region rows per 256-byte bank window
-      constexpr int RPI = kWave / RCH;                // rows per wavefront store
-      constexpr int NIT = (32 + RPI - 1) / RPI;       // stores per 32 rows
-      int8_t* region = (wave < kPerArr ? lds0 + wave * kRegion : lds1 + (wave - kPerArr) * kRegion);
-      // XOR swizzle of the 16-byte chunks for power-of-two row widths (the
-      // 96-channel rows of 192-wide tiles are read linearly instead)
-      auto rsw = [](int r, int c) { return kPow2 ? (c ^ ((r / RWIN) & (RCH - 1))) : c; };
-      const int n = n0 + wn * T::TN + (lane % RCH) * 8;   // this lane's 8 channels when storing
-      const bool lane_on = lane < RPI * RCH;
+  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
 #pragma unroll
-      for (int i = 0; i < T::FM; ++i) {
-        const int mb = m0 + wm * T::TM + i * 32;
+    for (int i = 0; i < T::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < T::FN; ++j) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            uint32_t wlo, whi;
-            outputs(i, j, g, sa_pre[i], wlo, whi);
-            *reinterpret_cast<u32x2*>(region + row_in * RB + rsw(row_in, 4 * j + g) * 16 + 8 * khalf) =
-                u32x2{wlo, whi};
-          }
-        }
-        v4i v[NIT];
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-          const int r = min(it * RPI + lane / RCH, 31);
-          v[it] = *reinterpret_cast<const v4i*>(region + r * RB + rsw(r, lane % RCH) * 16);
-        }
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-          const int r = it * RPI + lane / RCH;
-          const int m = mb + r;
-          if (lane_on && r < 32 && m < M && n < N)
-            *reinterpret_cast<v4i*>(reinterpret_cast<uint16_t*>(out) + (int64_t)m * ldy + n) = v[it];
-        }
+      for (int j = 0; j < T::FN; ++j) acc[i][j] = v16i{};
+
+    // ---- K loop ----
+    if constexpr (T::kSplit) {
+      const int KT6 = (KT + 5) / 6 * 6;   // padding stages read as zeros
+      for (int kt = 0; kt < KT6; kt += 6) {
+        step_split(cur, lds0, lds3, lds1, lds4, kt);
+        step_split(cur, lds1, lds4, lds2, lds3, kt + 1);
+        step_split(cur, lds2, lds3, lds0, lds4, kt + 2);
+        step_split(cur, lds0, lds4, lds1, lds3, kt + 3);
+        step_split(cur, lds1, lds3, lds2, lds4, kt + 4);
+        step_split(cur, lds2, lds4, lds0, lds3, kt + 5);
       }
     } else {
+#pragma unroll
+      for (int s = 0; s < T::S; ++s) issue(cur, ring[s], s);
+      wait_vmcnt<(T::S - 1) * T::D>();
+      barrier();
+      frag(ring[0], 0, 0);
+      const int KTr = (KT + T::S - 1) / T::S * T::S;   // padding stages read as zeros
+      for (int kt = 0; kt < KTr; kt += T::S) {
+        if constexpr (T::S == 2) {
+          step(cur, lds0, lds1, kt);
+          step(cur, lds1, lds0, kt + 1);
+        } else if constexpr (T::S == 3) {
+          step(cur, lds0, lds1, kt);
+          step(cur, lds1, lds2, kt + 1);
+          step(cur, lds2, lds0, kt + 2);
+        } else {
+          step(cur, lds0, lds1, kt);
+          step(cur, lds1, lds2, kt + 1);
+          step(cur, lds2, lds3, kt + 2);
+          step(cur, lds3, lds0, kt + 3);
+        }
+      }
+    }
+    wait_vmcnt<0>();
+    wait_lgkmcnt0();
+    barrier();   // every DMA and fragment read of this tile is done
+
+    const int m0 = cur.m0, n0 = cur.n0;
+    const int t_next = t + gridDim.x;
+    const bool has_next = t_next < ntiles;
+
+    // ---- epilogue: lane holds token m, channels n = base + 8*g + 4*khalf + 0..3 ----
+    if constexpr (EPI == Epilogue::kBf16ScaleBias) {
+      // Lane-derived epilogue addresses are recomputed per tile (the opaque
+      // copy of the lane id keeps them from being hoisted out of the tile
+      // loop, where they would occupy registers through the K loop).
+      int e_lane = lane;
+      asm volatile("" : "+v"(e_lane));
+      const int e_row = e_lane % 32, e_kh = e_lane / 32;
+      // Scales and bias are requested before the next tile's first DMAs so
+      // that their waits do not include those DMAs.
+      float sa[T::FM];
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i) sa[i] = sa_n[i];
+      const float sw_l = sw_n, b_l = b_n;
+      TileAddr nxt;
+      if (has_next) {
+        setup(t_next, nxt);
+        load_scalars(nxt);
+      }
+      if constexpr (T::kSplit) {
+        if (has_next) {
+          issue_x(nxt, lds0, 0);
+          issue_w(nxt, lds3, 0);
+        }
+      }
+      // The block's channel scales and bias (as fp32) go to LDS once, so each
+      // group of 4 outputs needs two 16-byte LDS reads instead of 8 global loads.
+      float* s_lds = reinterpret_cast<float*>(sb_arr);
+      float* b_lds = s_lds + T::BN;
+      if (tid < T::BN) {
+        s_lds[tid] = sw_l;
+        b_lds[tid] = b_l;
+      }
+      // LDS writes done, then a plain barrier: a full __syncthreads() fence
+      // would also wait for the next tile's requests in flight
+      wait_lgkmcnt0();
+      barrier();
+      // Column tiles j (32 channels) one at a time: the scales and biases of
+      // this lane's 16 channels of j are read from LDS once for all FM row
+      // tiles, and each 32x32 output tile is turned around in the
+      // wavefront's own 2 KB LDS region (32 rows of 64 bytes) so that a
+      // store instruction writes 16 whole 64-byte row pieces instead of 64
+      // scattered 8-byte ones.
+      int8_t* const region = reg_a + wave * kRegion;
+      // 16-byte chunk c of region row r sits at chunk c ^ ((r/4) % 4), and in
+      // rows 16..31 its two 8-byte halves are swapped: the writes (8 bytes
+      // for each of 32 rows per half-wavefront) then cover all 64 banks once,
+      // and the reads (16 bytes for 4 rows x 4 chunks per quarter-wavefront)
+      // fill one 256-byte window.
+      auto rsw = [](int r, int c) { return c ^ ((r >> 2) & 3); };
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j) {
+        const int nj = wn * T::TN + j * 32;   // first channel of column tile j in the block
+        f32x4 sv[4], bv[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          sv[g] = *reinterpret_cast<const f32x4*>(s_lds + nj + g * 8 + e_kh * 4);
+          bv[g] = *reinterpret_cast<const f32x4*>(b_lds + nj + g * 8 + e_kh * 4);
+        }
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i) {
+          // 4 bf16 outputs (two packed words) of run g: channels nj + 8g + 4*khalf + 0..3
+          uint32_t w[4][2];
+          const v16i& c = acc[i][j];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const bf16x2 lo = __builtin_convertvector(
+                (f32x2{dequant(c[g * 4], sa[i], sv[g][0], bv[g][0]),
+                       dequant(c[g * 4 + 1], sa[i], sv[g][1], bv[g][1])}), bf16x2);
+            const bf16x2 hi = __builtin_convertvector(
+                (f32x2{dequant(c[g * 4 + 2], sa[i], sv[g][2], bv[g][2]),
+                       dequant(c[g * 4 + 3], sa[i], sv[g][3], bv[g][3])}), bf16x2);
+            w[g][0] = __builtin_bit_cast(uint32_t, lo);
+            w[g][1] = __builtin_bit_cast(uint32_t, hi);
+          }
+          const int mb = m0 + wm * T::TM + i * 32;   // first token of row tile i
+          if (vec_store) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              *reinterpret_cast<u32x2*>(region + e_row * 64 + rsw(e_row, g) * 16 +
+                                        8 * (e_kh ^ (e_row >> 4))) = u32x2{w[g][0], w[g][1]};
+            v4i v[2];
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+              const int r = it * 16 + e_lane / 4;
+              v[it] = *reinterpret_cast<const v4i*>(region + r * 64 + rsw(r, e_lane % 4) * 16);
+            }
+            v[1] = v4i{v[1][2], v[1][3], v[1][0], v[1][1]};   // rows 16..31: halves swapped
+            const int n = n0 + nj + (e_lane % 4) * 8;   // this lane's 8 channels when storing
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+              const int m = mb + it * 16 + e_lane / 4;
+              if (m < M && n < N)
+                *reinterpret_cast<v4i*>(reinterpret_cast<uint16_t*>(out) + (int64_t)m * ldy + n) = v[it];
+            }
+          } else {
+            const int m = mb + e_row;
+            if (m < M) {
+              uint16_t* yrow = reinterpret_cast<uint16_t*>(out) + (int64_t)m * ldy;
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                const int n = n0 + nj + g * 8 + e_kh * 4;
+                const uint16_t h[4] = {(uint16_t)w[g][0], (uint16_t)(w[g][0] >> 16), (uint16_t)w[g][1],
+                                       (uint16_t)(w[g][1] >> 16)};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  if (n + e < N) yrow[n + e] = h[e];
+              }
+            }
+          }
+        }
+      }
+      if (has_next) cur = nxt;
+    } else {
+      TileAddr nxt;
+      if (has_next) setup(t_next, nxt);
+      if constexpr (T::kSplit) {
+        if (has_next) {
+          issue_x(nxt, lds0, 0);
+          issue_w(nxt, lds3, 0);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < T::FM; ++i) {
         const int m = m0 + wm * T::TM + i * 32 + row_in;
         if (m >= M) continue;
-        uint16_t* yrow = reinterpret_cast<uint16_t*>(out) + (int64_t)m * ldy;
-        const float sa = sa_pre[i];
+        int32_t* crow = reinterpret_cast<int32_t*>(out) + (int64_t)m * ldy;
 #pragma unroll
         for (int j = 0; j < T::FN; ++j) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            uint32_t wlo, whi;
-            outputs(i, j, g, sa, wlo, whi);
             const int n = n0 + wn * T::TN + j * 32 + g * 8 + khalf * 4;
-            const uint16_t h[4] = {(uint16_t)wlo, (uint16_t)(wlo >> 16), (uint16_t)whi,
-                                   (uint16_t)(whi >> 16)};
+            if (vec_store && n + 3 < N) {
+              *reinterpret_cast<v4i*>(crow + n) =
+                  v4i{acc[i][j][g * 4], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]};
+            } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (n + e < N) yrow[n + e] = h[e];
+              for (int e = 0; e < 4; ++e)
+                if (n + e < N) crow[n + e] = acc[i][j][g * 4 + e];
+            }
           }
         }
       }
+      if (has_next) cur = nxt;
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < T::FM; ++i) {
-      const int m = m0 + wm * T::TM + i * 32 + row_in;
-      if (m >= M) continue;
-      int32_t* crow = reinterpret_cast<int32_t*>(out) + (int64_t)m * ldy;
-#pragma unroll
-      for (int j = 0; j < T::FN; ++j) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * T::TN + j * 32 + g * 8 + khalf * 4;
-          if (vec_store && n + 3 < N) {
-            *reinterpret_cast<v4i*>(crow + n) =
-                v4i{acc[i][j][g * 4], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]};
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (n + e < N) crow[n + e] = acc[i][j][g * 4 + e];
-          }
-        }
+
+    // ---- hand over to the next tile ----
+    if (has_next) {
+      wait_lgkmcnt0();
+      barrier();   // the epilogue's LDS regions and scales are free again
+      if constexpr (T::kSplit) {
+        issue_x(cur, lds1, 1);
+        issue_w(cur, lds4, 1);
+        issue_x(cur, lds2, 2);
+        // everything older than these three requests -- the epilogue's
+        // stores and X_0, W_0 of the new tile -- has completed
+        wait_vmcnt<2 * T::DX + T::DW>();
+        barrier();
+        frag2(lds0, lds3, 0, 0);
       }
     }
   }
+}
+
+// Compute units of the current device (each persistent workgroup takes one).
+int num_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n / kNumXcd * kNumXcd > 0 ? n / kNumXcd * kNumXcd : n;
 }
 
 // Launch tile configuration T on the sub-problem M x N x K whose output rows
@@ -502,7 +598,9 @@ hipError_t launch_t(Epilogue epi, const int8_t* xq, const int8_t* wq, const floa
                     int64_t K, int64_t ldy, hipStream_t stream) {
   const int tiles_m = (int)((M + T::BM - 1) / T::BM);
   const int tiles_n = (int)((N + T::BN - 1) / T::BN);
-  const dim3 grid((unsigned)(tiles_m * tiles_n));
+  // at most one workgroup per CU (the tiles occupy a whole CU); a multiple
+  // of the 8 XCDs so that each workgroup stays on its XCD's tile range
+  const dim3 grid((unsigned)std::min<int64_t>((int64_t)tiles_m * tiles_n, num_cus()));
   const dim3 block(T::kThreads);
   const uintptr_t o = reinterpret_cast<uintptr_t>(out);
   if (epi == Epilogue::kBf16ScaleBias) {
