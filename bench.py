@@ -48,6 +48,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-rows", type=int, default=4096, help="tokens per linear in the CPU sample")
+    p.add_argument("--no-cold", action="store_true", help="skip the cold-cache GEMM / quantize timings")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="first run a plain 1 GiB streaming copy 3 times (the reference kernel "
+                        "for scaling HBM byte counters)")
     return p.parse_args()
 
 
@@ -56,8 +60,9 @@ def log(msg):
 
 
 def gemm_traffic():
-    """HBM bytes per GEMM launch measured with rocprofv3 counters, if they were
-    taken on the current kernel source (else None)."""
+    """HBM bytes (read + write, calibrated) of the four GEMM launches of one
+    step, measured with rocprofv3 counters, if they were taken on the current
+    kernel source (else None)."""
     try:
         rec = json.load(open(PROFILE_TRAFFIC))
     except (OSError, ValueError):
@@ -65,7 +70,37 @@ def gemm_traffic():
     digest = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
     if rec.get("gemm_source_sha256") != digest:
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get("bytes_per_step")
+
+
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration(dev):
+    """A plain streaming copy of known size (bitwise_not of 1 GiB of uint8:
+    reads and writes COPY_BYTES each): its byte counters give the factor
+    that turns counter readings into bytes."""
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def time_cold(fn, stream, scrub, reps=5):
+    """Median time of fn() with the caches flushed before each run (a 512 MB
+    write between runs evicts L2 and the 256 MB Infinity Cache)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(reps):
+        scrub.zero_()
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return float(np.median(ts))
 
 
 def cpu_baseline(rows: int) -> dict:
@@ -105,6 +140,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
+    if args.copy_calibration:
+        log(f"copy calibration: 3 x {COPY_BYTES} B streaming copy")
+        copy_calibration(dev)
 
     # ---- inputs, resident in HBM; weights quantized offline ----
     layers = []
@@ -190,11 +228,38 @@ def main():
     for p, t in zip(per, bf_ms):
         p["bf16_us"] = round(t * 1e3, 2)
 
+    # ---- cold caches: GEMM and quantize with L2 and Infinity Cache flushed ----
+    cold = None
+    if not args.no_cold:
+        log("cold-cache timings")
+        scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold = {}
+        for i, L in enumerate(layers):
+            s = L["shape"]
+            g = time_cold(lambda: w8.linear(L["xq"], L["xs"], L["wq"], L["ws"], L["b"], y=L["y"]), stream, scrub)
+            q = time_cold(lambda: w8.quantize_act(L["x"], L["xq"], L["xs"]), stream, scrub)
+            per[i]["gemm_cold_us"] = round(g * 1e3, 2)
+            per[i]["quant_cold_us"] = round(q * 1e3, 2)
+            per[i]["quant_cold_gbs"] = round((3 * s.M * s.K + 4 * s.M) / q / 1e6, 1)
+            cold[s.name] = (g, q)
+        del scrub
+        g_sum = sum(v[0] for v in cold.values())
+        q_sum = sum(v[1] for v in cold.values())
+        cold = {"gemm_tops": round(step_ops / g_sum / 1e9, 1),
+                "linear_tops": round(step_ops / (g_sum + q_sum) / 1e9, 1),
+                "quant_gbs": round(q_bytes / q_sum / 1e6, 1),
+                "note": "median of 5 runs per launch, 512 MB cache scrub before each"}
+
     traffic = gemm_traffic()
+    alg_bytes = sum(L["shape"].M * L["shape"].K + L["shape"].N * L["shape"].K
+                    + 2 * L["shape"].M * L["shape"].N + 4 * L["shape"].M + 4 * L["shape"].N
+                    + 2 * L["shape"].N for L in layers)
     roofline = {"bound": "mfma", "kernel": "gemm_i8_kernel (fused W8A8 linear)",
                 "achieved": round(gemm_tops, 1), "peak": MFMA_INT8_PEAK_TOPS, "unit": "TOPS",
                 "frac": round(gemm_tops / MFMA_INT8_PEAK_TOPS, 4), "traffic": traffic,
-                "per_launch": "sum of 2MNK over the four GEMM launches / sum of their mean durations"}
+                "algorithmic_bytes": alg_bytes,
+                "per_launch": "sum of 2MNK over the four GEMM launches / sum of their mean durations; "
+                              "traffic and algorithmic_bytes are summed over the same four launches"}
 
     result = {
         "metric": "fused W8A8 linear int8 TOPS and % of MI355X int8 MFMA peak; speedup vs bf16",
@@ -218,6 +283,7 @@ def main():
         "quantize": {"bound": "hbm", "achieved": round(q_bytes / q_total_ms / 1e6, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(q_bytes / q_total_ms / 1e6 / HBM_PEAK_GBS, 4)},
+        "cold": cold,
         "vs_bf16": {"bf16_torch_linear_tops": round(step_ops / bf_total / 1e9, 1),
                     "speedup_full_linear": round(bf_total / (gemm_total_ms + q_total_ms), 3),
                     "speedup_gemm_only": round(bf_total / gemm_total_ms, 3)},
