@@ -13,9 +13,13 @@ linears / step time.
 Besides the contract fields the JSON line carries the roofline of the
 dominant kernel (the GEMM, timed per launch with HIP events on its stream),
 the CPU oracle timed on a bounded sample on the host, the quantize kernel's
-HBM rate and a same-shape bf16 torch GEMM on the same GPU.
+HBM rate, cold-cache timings, the same linears through the dequantize-to-bf16
+path the method replaces, a same-shape bf16 torch GEMM, and the GEMM rates
+of the other workloads (768px attention projection and MLP pair, 1024px QKV
+with outlier channels).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--no-cold]
+                    [--no-other] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -49,6 +53,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-rows", type=int, default=4096, help="tokens per linear in the CPU sample")
     p.add_argument("--no-cold", action="store_true", help="skip the cold-cache GEMM / quantize timings")
+    p.add_argument("--no-other", action="store_true", help="skip timing the other workloads' linears")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run a plain 1 GiB streaming copy 3 times (the reference kernel "
                         "for scaling HBM byte counters)")
@@ -125,6 +130,52 @@ def cpu_baseline(rows: int) -> dict:
             "sample": f"first {rows} of {WORKLOAD.linears[0].M} tokens of each of the 4 linears "
                       f"(full N and K), quantize + int32 GEMM + fp32 dequant + bf16; "
                       f"{ops / 1e9:.1f} G int8 ops in {elapsed:.1f} s"}
+
+
+def time_other_workloads(w8, dev, stream, iters: int = 10) -> dict:
+    """Warm GEMM and quantize times of the other workloads' linears (the
+    768px attention projection and MLP pair, the 1024px QKV with outliers):
+    median of `iters` launches each, HIP events on the launch stream."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def med(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(iters):
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    out = {}
+    for wl in datagen.WORKLOADS[1:4]:
+        lin = []
+        for li, shape in enumerate(wl.linears):
+            if shape.act == "gelu_of_prev":   # timing only: any bf16 input of the shape
+                x = datagen.random_bf16((shape.M, shape.K), wl.seed * 100 + li).to(dev)
+            else:
+                x = datagen.gen_act(shape, wl.seed, li).to(dev)
+            wbf, b = datagen.gen_weight(shape, wl.seed, li)
+            wq, ws = w8.quantize_weight(wbf.to(dev))
+            b = b.to(dev)
+            xq, xs = w8.quantize_act(x)
+            y = torch.empty((shape.M, shape.N), dtype=torch.bfloat16, device=dev)
+            g = med(lambda: w8.linear(xq, xs, wq, ws, b, y=y))
+            q = med(lambda: w8.quantize_act(x, xq, xs))
+            ops = 2 * shape.M * shape.N * shape.K
+            lin.append({"linear": shape.name, "M": shape.M, "K": shape.K, "N": shape.N,
+                        "plan": w8.select_tile(shape.M, shape.N, shape.K),
+                        "gemm_us": round(g * 1e3, 2), "gemm_tops": round(ops / g / 1e9, 1),
+                        "quant_us": round(q * 1e3, 2)})
+        g_us = sum(l["gemm_us"] for l in lin)
+        q_us = sum(l["quant_us"] for l in lin)
+        out[wl.name] = {"gemm_tops": round(wl.ops / g_us / 1e6, 1),
+                        "frac": round(wl.ops / g_us / 1e6 / MFMA_INT8_PEAK_TOPS, 4),
+                        "linear_tops": round(wl.ops / (g_us + q_us) / 1e6, 1), "linears": lin}
+    return out
 
 
 def main():
@@ -250,6 +301,32 @@ def main():
                 "quant_gbs": round(q_bytes / q_sum / 1e6, 1),
                 "note": "median of 5 runs per launch, 512 MB cache scrub before each"}
 
+    # ---- the dequantize-to-bf16 path the method replaces (same int8 weights) ----
+    log("dequantize-to-bf16 comparator")
+    slow_ms = []
+    for L in layers:
+        scratch = {}
+        fn = lambda: w8.dequant_bf16_linear(L["x"], L["wq"], L["ws"], L["b"], scratch)
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(max(3, args.steps // 2)):
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        slow_ms.append(float(np.median(ts)))
+        del scratch
+    slow_total = sum(slow_ms)
+    for p, t in zip(per, slow_ms):
+        p["dequant_bf16_us"] = round(t * 1e3, 2)
+
+    other = None
+    if not args.no_other:
+        log("other workloads")
+        other = time_other_workloads(w8, dev, stream)
+
     traffic = gemm_traffic()
     alg_bytes = sum(L["shape"].M * L["shape"].K + L["shape"].N * L["shape"].K
                     + 2 * L["shape"].M * L["shape"].N + 4 * L["shape"].M + 4 * L["shape"].N
@@ -284,6 +361,10 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(q_bytes / q_total_ms / 1e6 / HBM_PEAK_GBS, 4)},
         "cold": cold,
+        "other_workloads": other,
+        "vs_dequant_bf16_path": {"tops": round(step_ops / slow_total / 1e9, 1),
+                                 "speedup_full_linear": round(slow_total / (gemm_total_ms + q_total_ms), 3),
+                                 "path": "quantize_act + dequantize X and W to bf16 + torch F.linear"},
         "vs_bf16": {"bf16_torch_linear_tops": round(step_ops / bf_total / 1e9, 1),
                     "speedup_full_linear": round(bf_total / (gemm_total_ms + q_total_ms), 3),
                     "speedup_gemm_only": round(bf_total / gemm_total_ms, 3)},

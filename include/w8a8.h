@@ -78,6 +78,20 @@ w8a8_status w8a8_quantize_act(const uint16_t *x, int64_t M, int64_t K,
                               int8_t *xq, float *x_scale, hipStream_t stream);
 
 /*
+ * Row-wise dequantization back to bf16 (the slow path's first step):
+ *   out[r,k] = bf16_rne( fl32( float(q[r,k]) * scale[r] ) )
+ * for q int8 [R,K] and scale fp32 [R]; out is bf16 [R,K].
+ * Abstract: the production "INT8" forward this work replaces quantizes
+ * weights and activations and then immediately dequantizes them to bf16 for a
+ * bf16 matrix multiply.  Provided so that path can be measured against the
+ * fused GEMM; it is not part of the fused path.  Shape contract as above
+ * (16 <= K, K % 16 == 0, R >= 0; R == 0 is a no-op); q and out 16-byte
+ * aligned, scale 4-byte aligned.
+ */
+w8a8_status w8a8_dequantize_rows(const int8_t *q, const float *scale, int64_t R, int64_t K,
+                                 uint16_t *out, hipStream_t stream);
+
+/*
  * Fused W8A8 linear: int8 GEMM with the dequant + bias epilogue.
  *   acc[m,n] = sum_k xq[m,k] * wq[n,k]                 (exact, int32)
  *   y[m,n]   = bf16_rne( fl32( fl32( fl32(float(acc[m,n]) * x_scale[m])

@@ -22,10 +22,14 @@ Functions:
   dequant_ref64       the same in fp64 (error-analysis reference)
   w8a8_linear_ref     the whole path, returning every intermediate
   gelu_ref            exact erf GELU in fp64 (glue of the MLP-pair workload)
+  dequant_rows_ref    int8 codes x row scale -> bf16 (the dequantize-to-bf16 path)
+  dequant_bf16_linear_ref  that whole path: quantize, dequantize, product in fp64
 """
 from .quant import bf16_to_f32, f32_to_bf16_bits, quantize_rows_ref
 from .gemm import int_gemm_ref
 from .dequant import dequant_ref, dequant_ref64, w8a8_linear_ref, gelu_ref
+from .slowpath import dequant_rows_ref, dequant_bf16_linear_ref
 
 __all__ = ["bf16_to_f32", "f32_to_bf16_bits", "quantize_rows_ref", "int_gemm_ref",
-           "dequant_ref", "dequant_ref64", "w8a8_linear_ref", "gelu_ref"]
+           "dequant_ref", "dequant_ref64", "w8a8_linear_ref", "gelu_ref",
+           "dequant_rows_ref", "dequant_bf16_linear_ref"]

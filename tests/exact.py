@@ -49,3 +49,31 @@ def rne_int(q: Fraction) -> int:
 
 def bf16_value(bits: int) -> float:
     return struct.unpack("<f", struct.pack("<I", (bits & 0xFFFF) << 16))[0]
+
+
+def round_to_bf16(q: Fraction) -> float:
+    """Round an exact rational to the nearest bfloat16 value, ties to even, with
+    gradual underflow.  From the format's definition: 8-bit significand (7
+    stored bits), the binary32 exponent range (minimum normal exponent -126),
+    subnormal spacing 2**-133."""
+    if q == 0:
+        return 0.0
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    if Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)
+    scaled = a * Fraction(2) ** (7 - e)
+    m = scaled.numerator // scaled.denominator
+    rem = scaled - m
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and m % 2 == 1):
+        m += 1
+    if m == 1 << 8:
+        m >>= 1
+        e += 1
+    if e > 127:
+        raise OverflowError
+    return sign * float(Fraction(m) * Fraction(2) ** (e - 7))

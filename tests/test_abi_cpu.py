@@ -105,3 +105,16 @@ def test_tile_table(w):
     assert w.lib.w8a8_tile_info(n, None, None, None, None) == 5
     for M, N, K in [(64, 128, 256), (2304, 3072, 3072), (4096, 9216, 3072), (8192, 3072, 12288), (1, 1, 16)]:
         assert 0 <= w.select_tile(M, N, K) < n
+
+
+def test_dequantize_validation(w):
+    f = w.lib.w8a8_dequantize_rows
+    assert f(None, A, 4, 64, A, None) == 1
+    assert f(A, None, 4, 64, A, None) == 1
+    assert f(A, A, 4, 64, None, None) == 1
+    for R, K in [(-1, 64), (4, 0), (4, 8), (4, 24), (4, 15)]:
+        assert f(A, A, R, K, A, None) == 2, (R, K)
+    assert f(A + 8, A, 4, 64, A, None) == 3
+    assert f(A, A + 2, 4, 64, A, None) == 3
+    assert f(A, A, 4, 64, A + 8, None) == 3
+    assert f(None, None, 0, 64, None, None) == 0   # empty: no-op

@@ -8,9 +8,10 @@ Ideogram 4.0" (arXiv 2606.14598).
 """
 from ._lib import LIB_PATH, MAX_K, W8A8Error, lib, status_str
 from .module import W8A8Linear
-from .ops import (gemm_i32, linear, num_tiles, quantize_act, quantize_weight, select_tile,
-                  tile_info)
+from .ops import (dequantize_rows, gemm_i32, linear, num_tiles, quantize_act, quantize_weight,
+                  select_tile, tile_info)
+from .slowpath import dequant_bf16_linear
 
-__all__ = ["LIB_PATH", "MAX_K", "W8A8Error", "W8A8Linear", "gemm_i32", "lib", "linear",
-           "num_tiles", "quantize_act", "quantize_weight", "select_tile", "status_str",
-           "tile_info"]
+__all__ = ["LIB_PATH", "MAX_K", "W8A8Error", "W8A8Linear", "dequant_bf16_linear",
+           "dequantize_rows", "gemm_i32", "lib", "linear", "num_tiles", "quantize_act",
+           "quantize_weight", "select_tile", "status_str", "tile_info"]

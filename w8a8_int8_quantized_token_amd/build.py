@@ -1,6 +1,6 @@
 """Build libw8a8.so (HIP, gfx950) in-tree with hipcc.
 
-Usage: python -m w8a8_int8_quantized_token_amd.build
+Usage: python w8a8_int8_quantized_token_amd/build.py
 """
 from __future__ import annotations
 
@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libw8a8.so")
-SOURCES = ["quantize_rows.hip", "gemm_i8.hip", "w8a8_api.hip"]
+SOURCES = ["quantize_rows.hip", "dequantize_rows.hip", "gemm_i8.hip", "w8a8_api.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -12,6 +12,11 @@ namespace w8a8 {
 hipError_t launch_quantize_rows(const uint16_t* x, int8_t* q, float* scale,
                                 int64_t R, int64_t K, hipStream_t stream);
 
+// Row-wise dequantization: out[r,k] = bf16(fl32(float(q[r,k]) * scale[r])),
+// q int8 [R,K] -> out bf16 bits [R,K].  Requires K % 16 == 0 and R > 0.
+hipError_t launch_dequantize_rows(const int8_t* q, const float* scale, uint16_t* out, int64_t R,
+                                  int64_t K, hipStream_t stream);
+
 // One compiled GEMM tile configuration.
 struct TileDesc {
   int block_m;   // rows of X (tokens) per workgroup

@@ -72,6 +72,16 @@ w8a8_status w8a8_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* x
   return quantize(x, M, K, xq, x_scale, stream);
 }
 
+w8a8_status w8a8_dequantize_rows(const int8_t* q, const float* scale, int64_t R, int64_t K,
+                                 uint16_t* out, hipStream_t stream) {
+  if (R < 0 || R > kMaxRows || K < 16 || K % 16 != 0 || K > kMaxQuantK) return W8A8_ERR_SHAPE;
+  if (R == 0) return W8A8_OK;
+  if (!q || !scale || !out) return W8A8_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(scale, 4) || !aligned(out, 16)) return W8A8_ERR_ALIGN;
+  return w8a8::launch_dequantize_rows(q, scale, out, R, K, stream) == hipSuccess ? W8A8_OK
+                                                                                 : W8A8_ERR_LAUNCH;
+}
+
 w8a8_status w8a8_linear_tile(const int8_t* xq, const float* x_scale, const int8_t* wq,
                              const float* w_scale, const uint16_t* bias, uint16_t* y, int64_t M,
                              int64_t N, int64_t K, int tile, hipStream_t stream) {

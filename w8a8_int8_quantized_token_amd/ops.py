@@ -55,6 +55,23 @@ def quantize_act(x: torch.Tensor, xq=None, x_scale=None):
     return _quant(lib.w8a8_quantize_act, x, xq, x_scale, "x")
 
 
+def dequantize_rows(q: torch.Tensor, scale: torch.Tensor, out=None):
+    """q int8 [R,K], scale fp32 [R] -> bf16 [R,K] = bf16(float(q) * scale[row])."""
+    _need(q, torch.int8, 2, "q")
+    _need(scale, torch.float32, 1, "scale")
+    R, K = q.shape
+    if scale.shape[0] != R:
+        raise ValueError("scale length does not match the rows of q")
+    if out is None:
+        out = torch.empty((R, K), dtype=torch.bfloat16, device=q.device)
+    _need(out, torch.bfloat16, 2, "out")
+    if tuple(out.shape) != (R, K):
+        raise ValueError("out shape does not match q")
+    check(lib.w8a8_dequantize_rows(q.data_ptr(), scale.data_ptr(), R, K, out.data_ptr(), _stream(q)),
+          "w8a8_dequantize_rows")
+    return out
+
+
 def _gemm_args(xq, wq):
     _need(xq, torch.int8, 2, "xq")
     _need(wq, torch.int8, 2, "wq")
