@@ -118,3 +118,14 @@ def test_dequantize_validation(w):
     assert f(A, A + 2, 4, 64, A, None) == 3
     assert f(A, A, 4, 64, A + 8, None) == 3
     assert f(None, None, 0, 64, None, None) == 0   # empty: no-op
+
+
+def test_plan_choice_on_dit_shapes(w):
+    """The cost model picks the plan that was fastest in sweeps over every
+    plan on MI355X for these shapes (ids: 0 256x256 split ring + 128x256
+    tail, 4 256x192, 5 128x256, 8 64x64)."""
+    best = {(8192, 9216, 3072): 4, (8192, 3072, 3072): 4, (8192, 12288, 3072): 0,
+            (8192, 3072, 12288): 4, (2304, 3072, 3072): 5, (2304, 12288, 3072): 0,
+            (2304, 3072, 12288): 5, (4096, 9216, 3072): 4, (64, 128, 256): 8}
+    for (M, N, K), plan in best.items():
+        assert w.select_tile(M, N, K) == plan, (M, N, K)

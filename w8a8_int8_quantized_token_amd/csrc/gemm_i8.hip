@@ -682,29 +682,67 @@ int64_t main_columns(const TileDesc& d, int64_t M, int64_t N) {
   return 0;
 }
 
+// Relative throughput of one CU running a configuration's tiles, against
+// the 256x256 split-ring tile (measured on MI355X at K = 3072 and 12288 on
+// the DiT shapes; the persistent grid runs one tile per CU at a time).
+double cfg_efficiency(int cfg) {
+  switch (cfg) {
+    case kSplit256: return 1.0;
+    case kWhole256: return 0.97;
+    case k192: return 1.0;
+    case kTail128x256: return 0.70;
+    case k256x128: return 0.63;
+    case k128: return 0.54;
+    default: return 0.27;
+  }
+}
+
+// Estimated time of one launch of `cfg` over an M x N x K problem, in units
+// of one 256x256 tile's K loop: whole rounds of 256 tiles (a partial round
+// costs as much as a full one), each as long as the tile's work over its
+// efficiency, with the zero-padded stages of the ring counted.
+double launch_cost(int cfg, int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0) return 0.0;
+  const TileDesc& d = kCfgs[cfg];
+  const int64_t tiles = ((M + d.block_m - 1) / d.block_m) * ((N + d.block_n - 1) / d.block_n);
+  const int64_t rounds = (tiles + kCUs - 1) / kCUs;
+  const int64_t kt = (K + d.block_k - 1) / d.block_k;
+  const int64_t ring = cfg == kSplit256 || cfg == k192 ? 6 : cfg == kWhole256 ? 2
+                       : cfg == kTail128x256 || cfg == k256x128 || cfg == k64 ? 3 : 4;
+  const double pad = (double)((kt + ring - 1) / ring * ring) / (double)kt;
+  return (double)rounds * (double)(d.block_m * d.block_n) / 65536.0 * pad / cfg_efficiency(cfg);
+}
+
+double plan_cost(int plan, int64_t M, int64_t N, int64_t K) {
+  const Plan& p = kPlans[plan];
+  const int64_t c = p.tail >= 0 ? main_columns(kCfgs[p.main], M, N) : 0;
+  if (c == 0) return launch_cost(p.main, M, N, K);
+  const int64_t nm = c * kCfgs[p.main].block_n;
+  return launch_cost(p.main, M, nm, K) + launch_cost(p.tail, M, N - nm, K);
+}
+
 }  // namespace
 
 int num_tiles() { return kNumPlans; }
 const TileDesc& tile_desc(int tile) { return kCfgs[kPlans[tile].main]; }
 
-// Shape -> plan, from sweeps over the DiT shapes on MI355X: 256x256 tiles with
-// 128-byte stages (plus the 128x256 tail) whenever they give every CU at least
-// one tile -- the split ring when K is a multiple of 6 stages or close enough
-// that its zero-padded stages cost < 5%; below that, 256x128, then 128x128,
-// then 64x64 tiles keep the 256 CUs busy.
+// Shape -> plan: the cheapest plan under the cost model above (ties go to
+// the earlier plan, i.e. to bigger tiles).  It reproduces the best plan of
+// sweeps over all plans on the DiT shapes (M = 2304, 4096, 8192 tokens;
+// K = 3072, 12288): 256x192 tiles where their count fills whole rounds
+// better than 256x256 ones, 128x256 tiles for 768px shapes with about a
+// hundred 256x256 tiles, 256x256 (plus the 128x256 tail) otherwise.
 int select_tile(int64_t M, int64_t N, int64_t K) {
-  auto tiles = [&](int cfg) {
-    return ((M + kCfgs[cfg].block_m - 1) / kCfgs[cfg].block_m) *
-           ((N + kCfgs[cfg].block_n - 1) / kCfgs[cfg].block_n);
-  };
-  if (tiles(kSplit256) >= kCUs) {
-    const int64_t kt = (K + 127) / 128;
-    const int64_t kt6 = (kt + 5) / 6 * 6;
-    return (kt6 - kt) * 20 <= kt ? 0 : 2;
+  int best = 0;
+  double best_cost = plan_cost(0, M, N, K);
+  for (int p = 1; p < kNumPlans; ++p) {
+    const double c = plan_cost(p, M, N, K);
+    if (c < best_cost * 0.999) {
+      best = p;
+      best_cost = c;
+    }
   }
-  if (tiles(k256x128) >= kCUs / 2) return 6;
-  if (tiles(k128) >= kCUs / 2) return 7;
-  return 8;
+  return best;
 }
 
 hipError_t launch_gemm(int tile, Epilogue epi, const int8_t* xq, const int8_t* wq,
