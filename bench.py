@@ -163,13 +163,22 @@ def time_other_workloads(w8, dev, stream, iters: int = 10) -> dict:
             b = b.to(dev)
             xq, xs = w8.quantize_act(x)
             y = torch.empty((shape.M, shape.N), dtype=torch.bfloat16, device=dev)
-            g = med(lambda: w8.linear(xq, xs, wq, ws, b, y=y))
+            feeds_gelu = li + 1 < len(wl.linears) and wl.linears[li + 1].act == "gelu_of_prev"
+            g = med(lambda: w8.linear(xq, xs, wq, ws, b, y=y, gelu=feeds_gelu))
             q = med(lambda: w8.quantize_act(x, xq, xs))
             ops = 2 * shape.M * shape.N * shape.K
-            lin.append({"linear": shape.name, "M": shape.M, "K": shape.K, "N": shape.N,
-                        "plan": w8.select_tile(shape.M, shape.N, shape.K),
-                        "gemm_us": round(g * 1e3, 2), "gemm_tops": round(ops / g / 1e9, 1),
-                        "quant_us": round(q * 1e3, 2)})
+            rec = {"linear": shape.name, "M": shape.M, "K": shape.K, "N": shape.N,
+                   "plan": w8.select_tile(shape.M, shape.N, shape.K),
+                   "gemm_us": round(g * 1e3, 2), "gemm_tops": round(ops / g / 1e9, 1),
+                   "quant_us": round(q * 1e3, 2)}
+            if feeds_gelu:
+                # the GELU before the next linear runs in this GEMM's epilogue; the
+                # unfused alternative is the plain epilogue plus a separate GELU pass
+                g0 = med(lambda: w8.linear(xq, xs, wq, ws, b, y=y))
+                glue = med(lambda: torch.nn.functional.gelu(y))
+                rec.update(gemm_gelu_epilogue_us=rec["gemm_us"], gemm_plain_us=round(g0 * 1e3, 2),
+                           separate_gelu_us=round(glue * 1e3, 2))
+            lin.append(rec)
         g_us = sum(l["gemm_us"] for l in lin)
         q_us = sum(l["quant_us"] for l in lin)
         out[wl.name] = {"gemm_tops": round(wl.ops / g_us / 1e6, 1),

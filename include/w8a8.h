@@ -107,6 +107,25 @@ w8a8_status w8a8_linear(const int8_t *xq, const float *x_scale, const int8_t *wq
                         int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 /*
+ * Fused W8A8 linear with GELU in the epilogue (the up-projection of a
+ * transformer MLP):
+ *   y[m,n] = bf16_rne( gelu( fl32 value of w8a8_linear above ) ),
+ *   gelu(v) = v * Phi(v) (exact erf definition), evaluated in fp32 with a
+ *   relative error below 2e-5 (below 1e-6 where |gelu| > 0.01).
+ * Abstract: the per-token x per-channel dequantization and the bias are
+ * folded into the GEMM epilogue; the activation that follows the linear is
+ * folded in the same way, so the pre-activation never reaches memory.  Not
+ * bit-reproducible against an fp64 GELU: compare with a tolerance.  Same
+ * arguments, contracts and errors as w8a8_linear / w8a8_linear_tile.
+ */
+w8a8_status w8a8_linear_gelu(const int8_t *xq, const float *x_scale, const int8_t *wq,
+                             const float *w_scale, const uint16_t *bias, uint16_t *y,
+                             int64_t M, int64_t N, int64_t K, hipStream_t stream);
+w8a8_status w8a8_linear_gelu_tile(const int8_t *xq, const float *x_scale, const int8_t *wq,
+                                  const float *w_scale, const uint16_t *bias, uint16_t *y,
+                                  int64_t M, int64_t N, int64_t K, int tile, hipStream_t stream);
+
+/*
  * Diagnostic entry: the same GEMM main loop, storing the raw int32
  * accumulators acc [M,N] instead of running the epilogue.
  * Abstract: the int8 x int8 -> int32 accumulation is checked bit for bit.

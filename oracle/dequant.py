@@ -11,7 +11,7 @@ same expression is kept as the error-analysis reference.
 from __future__ import annotations
 
 import numpy as np
-from scipy.special import erf
+from scipy.special import erfc
 
 from .gemm import int_gemm_ref
 from .quant import bf16_to_f32, f32_to_bf16_bits, quantize_rows_ref
@@ -58,6 +58,8 @@ def w8a8_linear_ref(x, w, bias=None, wq=None, s_w=None) -> dict:
 
 
 def gelu_ref(y) -> np.ndarray:
-    """Exact (erf) GELU, 0.5 * y * (1 + erf(y / sqrt(2))), in fp64."""
+    """Exact (erf) GELU, y * Phi(y) = 0.5 * y * (1 + erf(y / sqrt(2))), in fp64,
+    evaluated as 0.5 * y * erfc(-y / sqrt(2)) so that the tail y << 0 keeps its
+    relative accuracy (1 + erf cancels there)."""
     y = np.asarray(y, dtype=np.float64)
-    return 0.5 * y * (1.0 + erf(y / np.sqrt(2.0)))
+    return 0.5 * y * erfc(-y / np.sqrt(2.0))

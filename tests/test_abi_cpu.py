@@ -62,8 +62,9 @@ def test_quantize_validation(w, fn):
     assert f(None, 0, 64, None, None, None) == 0
 
 
-def test_linear_validation(w):
-    L = w.lib.w8a8_linear
+@pytest.mark.parametrize("fn", ["w8a8_linear", "w8a8_linear_gelu"])
+def test_linear_validation(w, fn):
+    L = getattr(w.lib, fn)
     args = lambda **k: [k.get(n, A) for n in ("xq", "sx", "wq", "sw", "b", "y")] + \
         [k.get("M", 8), k.get("N", 8), k.get("K", 64), None]
     assert L(*args(xq=None)) == 1

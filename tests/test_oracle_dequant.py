@@ -87,6 +87,15 @@ def test_gelu_values():
     assert abs(g[3] - 8.0) < 1e-12 and abs(g[4]) < 1e-12
 
 
+def test_gelu_tail_and_symmetry():
+    # Phi(-10) = 7.619853024160527e-24 (standard normal tail, 10 sigma)
+    g = gelu_ref(np.array([-10.0]))[0]
+    assert abs(g / (-10.0 * 7.619853024160527e-24) - 1.0) < 1e-12
+    # gelu(v) - gelu(-v) = v * (Phi(v) + Phi(-v)) = v
+    v = np.linspace(-6, 6, 97)
+    assert np.allclose(gelu_ref(v) - gelu_ref(-v), v, rtol=0, atol=1e-14)
+
+
 def test_whole_path_brute_force_tiny():
     """Every stage re-derived with exact rationals and explicit fp32 / bf16
     rounding, on tiny inputs."""

@@ -96,18 +96,54 @@ def test_workload(w, idx):
         run_linear_check(w, x, W, b, rows, label=f"{wl.name}/{shape.name}")
 
 
+def run_gelu_check(w, x_cpu, W_cpu, b_cpu, rows=None, tile=-1, label=""):
+    """Quantize + GEMM + dequant + GELU epilogue on the GPU against the oracle's
+    fp32 dequant followed by the fp64 GELU: bf16 tolerance, and no element more
+    than one bf16 ulp from bf16(gelu(y32))."""
+    _log(f"[parity] gelu {label} M,K={tuple(x_cpu.shape)} N={W_cpu.shape[0]} tile={tile}")
+    M = x_cpu.shape[0]
+    rows = np.arange(M) if rows is None else rows
+    _, wq, ws = gpu_quant(w, W_cpu, weight=True)
+    _, xq, xs = gpu_quant(w, x_cpu)
+    bd = None if b_cpu is None else b_cpu.to(DEV)
+    h = w.linear(xq, xs, wq, ws, bd, tile=tile, gelu=True)
+    torch.cuda.synchronize()
+    ref_wq, ref_ws = quantize_rows_ref(W_cpu)
+    ref_xq, ref_xs = quantize_rows_ref(x_cpu[torch.from_numpy(rows)])
+    y32 = dequant_ref(int_gemm_ref(ref_xq, ref_wq), ref_xs, ref_ws, b_cpu)
+    g64 = gelu_ref(y32)
+    hb = bf16_bits(h.index_select(0, torch.from_numpy(rows).to(DEV)))
+    m = assert_bf16_close(hb, g64)
+    # one bf16 ulp at most from the correctly rounded fp64 GELU
+    want = f32_to_bf16_bits(g64.astype(np.float32)).astype(np.int32)
+    got = hb.astype(np.int32)
+    big = np.abs(g64) >= 1e-30   # below that the fp32 exp underflows: compared by tolerance only
+    assert np.all((((want ^ got) & 0x8000) == 0)[big])
+    assert int(np.max(np.abs((got & 0x7FFF) - (want & 0x7FFF))[big], initial=0)) <= 1
+    _log(f"[parity] gelu {label} ok cos={m['cos']:.7f} rel={m['rel']:.2e}")
+    return h
+
+
 def test_mlp_pair_stagewise(w):
-    """Up-projection, GELU (glue, applied on the host in fp64 and rounded to
-    bf16), then the down-projection re-quantized per token on the GPU."""
+    """Up-projection with the GELU epilogue, then the down-projection on the
+    GPU's own GELU output, re-quantized per token (stage-wise parity)."""
     wl = datagen.WORKLOADS[2]
     up, down = wl.linears
     x = datagen.gen_act(up, wl.seed, 0)
     Wu, bu = datagen.gen_weight(up, wl.seed, 0)
     Wd, bd = datagen.gen_weight(down, wl.seed, 1)
     rows = sample_rows(up.M, 48, 2000)
-    y_up, _, _ = run_linear_check(w, x, Wu, bu, rows, label="mlp_up")
-    h = torch.from_numpy(gelu_ref(bf16_to_f32(y_up.cpu())).astype(np.float32)).to(torch.bfloat16)
-    run_linear_check(w, h, Wd, bd, rows, label="mlp_down")
+    h = run_gelu_check(w, x, Wu, bu, rows, label="mlp_up")
+    run_linear_check(w, h.cpu(), Wd, bd, rows, label="mlp_down")
+
+
+@pytest.mark.parametrize("M,N,K", [(2, 3, 16), (65, 64, 1040), (257, 260, 3072), (129, 255, 12288)])
+def test_gelu_epilogue_ragged(w, M, N, K):
+    x = datagen.random_bf16((M, K), seed=M + 70)
+    W = datagen.random_bf16((N, K), seed=N + 110, std=0.02)
+    b = datagen.random_bf16((N,), seed=K + 1, std=0.5)
+    for tile in range(w.num_tiles()):
+        run_gelu_check(w, x, W, b, tile=tile, label=f"ragged tile{tile}")
 
 
 # ---------------------------------------------------------------- edge cases

@@ -38,6 +38,8 @@ def _load() -> ctypes.CDLL:
         "w8a8_select_tile": (i32, [i64, i64, i64]),
         "w8a8_linear_tile": (st, [p, p, p, p, p, p, i64, i64, i64, i32, p]),
         "w8a8_gemm_i32_tile": (st, [p, p, p, i64, i64, i64, i32, p]),
+        "w8a8_linear_gelu": (st, [p, p, p, p, p, p, i64, i64, i64, p]),
+        "w8a8_linear_gelu_tile": (st, [p, p, p, p, p, p, i64, i64, i64, i32, p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)

@@ -123,6 +123,33 @@ __device__ __forceinline__ float dequant(int acc, float sa, float sw, float b) {
   return __fadd_rn(__fmul_rn(__fmul_rn((float)acc, sa), sw), b);
 }
 
+// GELU with the exact (erf) definition, gelu(v) = v * Phi(v), where the
+// normal CDF is Phi(v) = 1 - erfc(v/sqrt2)/2 for v >= 0 and erfc(|v|/sqrt2)/2
+// below.  erfc(z), z >= 0, is the Chebyshev-fitted formula "erfcc" of
+// Numerical Recipes (2nd ed., section 6.2): t = 1/(1 + z/2),
+// erfc = t * exp(-z^2 + P(t)) with a degree-9 polynomial P whose fractional
+// error is below 1.2e-7.  Evaluated in fp32 (the exp argument's rounding
+// dominates for large z) the GELU has a relative error below 2e-5 for
+// |gelu| > 1e-30 and below 1e-6 where |gelu| > 0.01 -- far below the bf16
+// rounding of the stored result (the hardware reciprocal's 1-ulp error adds
+// about 1e-7).  Branch-free: one reciprocal, one exp.
+__device__ __forceinline__ float gelu(float v) {
+  const float z = fabsf(v) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, z, 1.0f));   // v_rcp_f32 (1 ulp)
+  float p = 0.17087277f;
+  p = fmaf(p, t, -0.82215223f);
+  p = fmaf(p, t, 1.48851587f);
+  p = fmaf(p, t, -1.13520398f);
+  p = fmaf(p, t, 0.27886807f);
+  p = fmaf(p, t, -0.18628806f);
+  p = fmaf(p, t, 0.09678418f);
+  p = fmaf(p, t, 0.37409196f);
+  p = fmaf(p, t, 1.00002368f);
+  p = fmaf(p, t, -1.26551223f);
+  const float half_erfc = 0.5f * t * __expf(fmaf(-z, z, p));
+  return v * (v >= 0.0f ? 1.0f - half_erfc : half_erfc);
+}
+
 // s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding).
 template <int n>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -340,7 +367,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
   // holds, and (threads below BN) one channel's scale and bias.
   float sa_n[T::FM], sw_n = 0.0f, b_n = 0.0f;
   auto load_scalars = [&](const TileAddr& a) {
-    if constexpr (EPI == Epilogue::kBf16ScaleBias) {
+    if constexpr (EPI != Epilogue::kRawI32) {
 #pragma unroll
       for (int i = 0; i < T::FM; ++i) sa_n[i] = sx[min(a.m0 + wm * T::TM + i * 32 + row_in, M - 1)];
       static_assert(T::BN <= T::kThreads, "one thread per channel of the block");
@@ -418,7 +445,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     const bool has_next = t_next < ntiles;
 
     // ---- epilogue: lane holds token m, channels n = base + 8*g + 4*khalf + 0..3 ----
-    if constexpr (EPI == Epilogue::kBf16ScaleBias) {
+    if constexpr (EPI != Epilogue::kRawI32) {
       // Lane-derived epilogue addresses are recomputed per tile (the opaque
       // copy of the lane id keeps them from being hoisted out of the tile
       // loop, where they would occupy registers through the K loop).
@@ -481,14 +508,18 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
           // 4 bf16 outputs (two packed words) of run g: channels nj + 8g + 4*khalf + 0..3
           uint32_t w[4][2];
           const v16i& c = acc[i][j];
+          // the fp32 output value (GELU applied for the gelu epilogue)
+          auto val = [&](int e, float s_w, float b) {
+            const float y = dequant(c[e], sa[i], s_w, b);
+            if constexpr (EPI == Epilogue::kBf16GeluScaleBias) return gelu(y);
+            else return y;
+          };
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const bf16x2 lo = __builtin_convertvector(
-                (f32x2{dequant(c[g * 4], sa[i], sv[g][0], bv[g][0]),
-                       dequant(c[g * 4 + 1], sa[i], sv[g][1], bv[g][1])}), bf16x2);
+                (f32x2{val(g * 4, sv[g][0], bv[g][0]), val(g * 4 + 1, sv[g][1], bv[g][1])}), bf16x2);
             const bf16x2 hi = __builtin_convertvector(
-                (f32x2{dequant(c[g * 4 + 2], sa[i], sv[g][2], bv[g][2]),
-                       dequant(c[g * 4 + 3], sa[i], sv[g][3], bv[g][3])}), bf16x2);
+                (f32x2{val(g * 4 + 2, sv[g][2], bv[g][2]), val(g * 4 + 3, sv[g][3], bv[g][3])}), bf16x2);
             w[g][0] = __builtin_bit_cast(uint32_t, lo);
             w[g][1] = __builtin_bit_cast(uint32_t, hi);
           }
@@ -608,6 +639,11 @@ hipError_t launch_t(Epilogue epi, const int8_t* xq, const int8_t* wq, const floa
     hipLaunchKernelGGL((gemm_i8_kernel<T, Epilogue::kBf16ScaleBias>), grid, block, 0, stream, xq,
                        wq, sx, sw, bias, out, (int)M, (int)N, (int)K, (int)ldy, tiles_m, tiles_n,
                        vec);
+  } else if (epi == Epilogue::kBf16GeluScaleBias) {
+    const int vec = (ldy % 8 == 0) && (o % 16 == 0);
+    hipLaunchKernelGGL((gemm_i8_kernel<T, Epilogue::kBf16GeluScaleBias>), grid, block, 0, stream,
+                       xq, wq, sx, sw, bias, out, (int)M, (int)N, (int)K, (int)ldy, tiles_m,
+                       tiles_n, vec);
   } else {
     const int vec = (ldy % 4 == 0) && (o % 16 == 0);
     hipLaunchKernelGGL((gemm_i8_kernel<T, Epilogue::kRawI32>), grid, block, 0, stream, xq, wq,
@@ -755,7 +791,7 @@ hipError_t launch_gemm(int tile, Epilogue epi, const int8_t* xq, const int8_t* w
   const int64_t nm = c * kCfgs[p.main].block_n;   // channels done by the main tiles
   hipError_t e = launch_cfg(p.main, epi, xq, wq, sx, sw, bias, out, M, nm, K, N, stream);
   if (e != hipSuccess) return e;
-  const size_t esz = epi == Epilogue::kBf16ScaleBias ? 2 : 4;
+  const size_t esz = epi == Epilogue::kRawI32 ? 4 : 2;
   void* out_tail = static_cast<char*>(out) + nm * esz;
   return launch_cfg(p.tail, epi, xq, wq + nm * K, sx, sw ? sw + nm : nullptr,
                     bias ? bias + nm : nullptr, out_tail, M, N - nm, K, N, stream);

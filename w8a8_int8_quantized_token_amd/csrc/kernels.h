@@ -29,11 +29,13 @@ int num_tiles();
 const TileDesc& tile_desc(int tile);
 int select_tile(int64_t M, int64_t N, int64_t K);
 
-enum class Epilogue { kBf16ScaleBias, kRawI32 };
+// kBf16ScaleBias: y = bf16(((acc*sx)*sw)+b); kBf16GeluScaleBias: the same
+// value through GELU before the bf16 rounding; kRawI32: the accumulators.
+enum class Epilogue { kBf16ScaleBias, kBf16GeluScaleBias, kRawI32 };
 
 // int8 GEMM acc[m,n] = sum_k xq[m,k] * wq[n,k] with the chosen epilogue.
-// For kBf16ScaleBias `out` is bf16 [M,N] and sx/sw/bias are used (bias may
-// be null); for kRawI32 `out` is int32 [M,N].  Shapes already validated.
+// For the bf16 epilogues `out` is bf16 [M,N] and sx/sw/bias are used (bias
+// may be null); for kRawI32 `out` is int32 [M,N].  Shapes already validated.
 hipError_t launch_gemm(int tile, Epilogue epi, const int8_t* xq, const int8_t* wq,
                        const float* sx, const float* sw, const uint16_t* bias, void* out,
                        int64_t M, int64_t N, int64_t K, hipStream_t stream);

@@ -82,9 +82,13 @@ w8a8_status w8a8_dequantize_rows(const int8_t* q, const float* scale, int64_t R,
                                                                                  : W8A8_ERR_LAUNCH;
 }
 
-w8a8_status w8a8_linear_tile(const int8_t* xq, const float* x_scale, const int8_t* wq,
-                             const float* w_scale, const uint16_t* bias, uint16_t* y, int64_t M,
-                             int64_t N, int64_t K, int tile, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+w8a8_status linear_epi(w8a8::Epilogue epi, const int8_t* xq, const float* x_scale,
+                       const int8_t* wq, const float* w_scale, const uint16_t* bias, uint16_t* y,
+                       int64_t M, int64_t N, int64_t K, int tile, hipStream_t stream) {
   w8a8_status st = check_gemm_shape(M, N, K);
   if (st != W8A8_OK) return st;
   const int t = resolve_tile(tile, M, N, K);
@@ -96,16 +100,40 @@ w8a8_status w8a8_linear_tile(const int8_t* xq, const float* x_scale, const int8_
   if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(y, 2) ||
       (bias && !aligned(bias, 2)))
     return W8A8_ERR_ALIGN;
-  return w8a8::launch_gemm(t, w8a8::Epilogue::kBf16ScaleBias, xq, wq, x_scale, w_scale, bias, y,
-                           M, N, K, stream) == hipSuccess
+  return w8a8::launch_gemm(t, epi, xq, wq, x_scale, w_scale, bias, y, M, N, K, stream) ==
+                 hipSuccess
              ? W8A8_OK
              : W8A8_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+w8a8_status w8a8_linear_tile(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                             const float* w_scale, const uint16_t* bias, uint16_t* y, int64_t M,
+                             int64_t N, int64_t K, int tile, hipStream_t stream) {
+  return linear_epi(w8a8::Epilogue::kBf16ScaleBias, xq, x_scale, wq, w_scale, bias, y, M, N, K,
+                    tile, stream);
 }
 
 w8a8_status w8a8_linear(const int8_t* xq, const float* x_scale, const int8_t* wq,
                         const float* w_scale, const uint16_t* bias, uint16_t* y, int64_t M,
                         int64_t N, int64_t K, hipStream_t stream) {
   return w8a8_linear_tile(xq, x_scale, wq, w_scale, bias, y, M, N, K, -1, stream);
+}
+
+w8a8_status w8a8_linear_gelu_tile(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                                  const float* w_scale, const uint16_t* bias, uint16_t* y,
+                                  int64_t M, int64_t N, int64_t K, int tile, hipStream_t stream) {
+  return linear_epi(w8a8::Epilogue::kBf16GeluScaleBias, xq, x_scale, wq, w_scale, bias, y, M, N,
+                    K, tile, stream);
+}
+
+w8a8_status w8a8_linear_gelu(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                             const float* w_scale, const uint16_t* bias, uint16_t* y, int64_t M,
+                             int64_t N, int64_t K, hipStream_t stream) {
+  return w8a8_linear_gelu_tile(xq, x_scale, wq, w_scale, bias, y, M, N, K, -1, stream);
 }
 
 w8a8_status w8a8_gemm_i32_tile(const int8_t* xq, const int8_t* wq, int32_t* acc, int64_t M,

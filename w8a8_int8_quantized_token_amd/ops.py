@@ -82,8 +82,9 @@ def _gemm_args(xq, wq):
     return M, N, K
 
 
-def linear(xq, x_scale, wq, w_scale, bias=None, y=None, tile: int = -1):
-    """Fused W8A8 linear: bf16 y [M,N] = dequant(xq @ wq^T) + bias."""
+def linear(xq, x_scale, wq, w_scale, bias=None, y=None, tile: int = -1, gelu: bool = False):
+    """Fused W8A8 linear: bf16 y [M,N] = dequant(xq @ wq^T) + bias (through
+    GELU before the bf16 rounding when ``gelu``)."""
     M, N, K = _gemm_args(xq, wq)
     _need(x_scale, torch.float32, 1, "x_scale")
     _need(w_scale, torch.float32, 1, "w_scale")
@@ -100,8 +101,9 @@ def linear(xq, x_scale, wq, w_scale, bias=None, y=None, tile: int = -1):
     _need(y, torch.bfloat16, 2, "y")
     if tuple(y.shape) != (M, N):
         raise ValueError("y shape does not match [M,N]")
-    check(lib.w8a8_linear_tile(xq.data_ptr(), x_scale.data_ptr(), wq.data_ptr(), w_scale.data_ptr(),
-                               bptr, y.data_ptr(), M, N, K, tile, _stream(xq)), "w8a8_linear")
+    fn = lib.w8a8_linear_gelu_tile if gelu else lib.w8a8_linear_tile
+    check(fn(xq.data_ptr(), x_scale.data_ptr(), wq.data_ptr(), w_scale.data_ptr(), bptr, y.data_ptr(),
+             M, N, K, tile, _stream(xq)), fn.__name__)
     return y
 
 
