@@ -187,6 +187,45 @@ def time_other_workloads(w8, dev, stream, iters: int = 10) -> dict:
     return out
 
 
+def time_fp8_variant(w8, layers, stream, iters: int = 10) -> dict:
+    """The same step with e4m3 codes (the fp8 variant): per linear, the fp8
+    activation quantizer and the fp8 GEMM with the same epilogue; weights
+    quantized to e4m3 once, before timing.  Median of `iters` launches."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def med(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(iters):
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    per, g_tot, q_tot, ops_tot = [], 0.0, 0.0, 0
+    for L in layers:
+        s = L["shape"]
+        cw, sw = w8.quantize_weight_fp8(L["wbf"])
+        cx, sx = w8.quantize_act_fp8(L["x"])
+        g = med(lambda: w8.linear_fp8(cx, sx, cw, sw, L["b"], y=L["y"]))
+        q = med(lambda: w8.quantize_act_fp8(L["x"], cx, sx))
+        ops = 2 * s.M * s.N * s.K
+        per.append({"linear": s.name, "gemm_us": round(g * 1e3, 2), "gemm_tops": round(ops / g / 1e9, 1),
+                    "quant_us": round(q * 1e3, 2)})
+        g_tot += g
+        q_tot += q
+        ops_tot += ops
+        del cw, cx
+    return {"gemm_tops": round(ops_tot / g_tot / 1e9, 1),
+            "frac_of_fp8_peak": round(ops_tot / g_tot / 1e9 / MFMA_INT8_PEAK_TOPS, 4),
+            "linear_tops": round(ops_tot / (g_tot + q_tot) / 1e9, 1), "per_linear": per,
+            "note": "e4m3 codes, v_mfma_f32_32x32x64_f8f6f4, same tiles and epilogue; "
+                    "MI355X dense fp8 peak = int8 peak = 5.0 P"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -331,6 +370,9 @@ def main():
     for p, t in zip(per, slow_ms):
         p["dequant_bf16_us"] = round(t * 1e3, 2)
 
+    log("fp8 variant")
+    fp8 = time_fp8_variant(w8, layers, stream)
+
     other = None
     if not args.no_other:
         log("other workloads")
@@ -371,6 +413,7 @@ def main():
                      "frac": round(q_bytes / q_total_ms / 1e6 / HBM_PEAK_GBS, 4)},
         "cold": cold,
         "other_workloads": other,
+        "fp8_variant": fp8,
         "vs_dequant_bf16_path": {"tops": round(step_ops / slow_total / 1e9, 1),
                                  "speedup_full_linear": round(slow_total / (gemm_total_ms + q_total_ms), 3),
                                  "path": "quantize_act + dequantize X and W to bf16 + torch F.linear"},

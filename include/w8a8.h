@@ -78,6 +78,35 @@ w8a8_status w8a8_quantize_act(const uint16_t *x, int64_t M, int64_t K,
                               int8_t *xq, float *x_scale, hipStream_t stream);
 
 /*
+ * The fp8 variant of the method (OCP e4m3 codes instead of int8; the pages
+ * weigh the int8 path against fp8 alternatives, here the same kernels run
+ * both on one GPU).  Codes are uint8 bit patterns of e4m3 (1 sign, 4
+ * exponent bits with bias 7, 3 mantissa bits; largest value 448).
+ *   quantize:  s = fl32(amax / 448), q = e4m3(fl32(v / s)) (nearest, ties to
+ *              even, saturating at +-448); an all-zero row gives s = 0, q = 0.
+ *   GEMM:      acc[m,n] = sum_k x[m,k] * w[n,k] accumulated in fp32 on the
+ *              matrix cores (exact products; the summation order is the
+ *              hardware's, within gamma_K * sum |x w| of the exact sum).
+ *   linear:    the same epilogue as w8a8_linear on the fp32 accumulators.
+ * Same shape, alignment and error contracts as the int8 entry points; the
+ * raw entry writes fp32 accumulators.
+ */
+w8a8_status w8a8_quantize_weight_fp8(const uint16_t *w, int64_t N, int64_t K, uint8_t *wq,
+                                     float *w_scale, hipStream_t stream);
+w8a8_status w8a8_quantize_act_fp8(const uint16_t *x, int64_t M, int64_t K, uint8_t *xq,
+                                  float *x_scale, hipStream_t stream);
+w8a8_status w8a8_linear_fp8(const uint8_t *xq, const float *x_scale, const uint8_t *wq,
+                            const float *w_scale, const uint16_t *bias, uint16_t *y,
+                            int64_t M, int64_t N, int64_t K, hipStream_t stream);
+w8a8_status w8a8_linear_fp8_tile(const uint8_t *xq, const float *x_scale, const uint8_t *wq,
+                                 const float *w_scale, const uint16_t *bias, uint16_t *y,
+                                 int64_t M, int64_t N, int64_t K, int tile, hipStream_t stream);
+w8a8_status w8a8_gemm_f32_fp8(const uint8_t *xq, const uint8_t *wq, float *acc,
+                              int64_t M, int64_t N, int64_t K, hipStream_t stream);
+w8a8_status w8a8_gemm_f32_fp8_tile(const uint8_t *xq, const uint8_t *wq, float *acc,
+                                   int64_t M, int64_t N, int64_t K, int tile, hipStream_t stream);
+
+/*
  * Row-wise dequantization back to bf16 (the slow path's first step):
  *   out[r,k] = bf16_rne( fl32( float(q[r,k]) * scale[r] ) )
  * for q int8 [R,K] and scale fp32 [R]; out is bf16 [R,K].

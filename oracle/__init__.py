@@ -24,7 +24,7 @@ Functions:
   gelu_ref            exact erf GELU in fp64 (glue of the MLP-pair workload)
   dequant_rows_ref    int8 codes x row scale -> bf16 (the dequantize-to-bf16 path)
   dequant_bf16_linear_ref  that whole path: quantize, dequantize, product in fp64
-  quantize_rows_fp8_ref, fp8_gemm_ref, fp32_sum_bound, w8a8_fp8_linear_ref
+  quantize_rows_fp8_ref, fp8_gemm_ref, fp32_sum_bound, fp8_mfma_bound, w8a8_fp8_linear_ref
                       the fp8 (e4m3) variant of the method (module oracle.fp8)
 """
 from .quant import bf16_to_f32, f32_to_bf16_bits, quantize_rows_ref
@@ -32,10 +32,10 @@ from .gemm import int_gemm_ref
 from .dequant import dequant_ref, dequant_ref64, w8a8_linear_ref, gelu_ref
 from .slowpath import dequant_rows_ref, dequant_bf16_linear_ref
 from .fp8 import (e4m3_decode, e4m3_encode, e4m3_round, fp32_sum_bound, fp8_gemm_ref,
-                  quantize_rows_fp8_ref, w8a8_fp8_linear_ref)
+                  fp8_mfma_bound, quantize_rows_fp8_ref, w8a8_fp8_linear_ref)
 
 __all__ = ["bf16_to_f32", "f32_to_bf16_bits", "quantize_rows_ref", "int_gemm_ref",
            "dequant_ref", "dequant_ref64", "w8a8_linear_ref", "gelu_ref",
            "dequant_rows_ref", "dequant_bf16_linear_ref", "e4m3_decode", "e4m3_encode",
-           "e4m3_round", "fp32_sum_bound", "fp8_gemm_ref", "quantize_rows_fp8_ref",
+           "e4m3_round", "fp32_sum_bound", "fp8_gemm_ref", "fp8_mfma_bound", "quantize_rows_fp8_ref",
            "w8a8_fp8_linear_ref"]

@@ -14,9 +14,10 @@ Readings taken (the pages give no fp8 recipe):
     saturating at +-448 (|v/s| <= 448 up to one fp32 rounding, so saturation
     only guards that rounding); an all-zero row gives s = 0 and zero codes;
   * the accumulation is exact here (fp64: every e4m3 x e4m3 product and every
-    partial sum of K <= 133144 of them is representable); a GPU accumulates
-    in fp32 and is held to the standard bound for that, |acc - exact| <=
-    gamma_K * sum_k |x_k w_k| with gamma_K = K u / (1 - K u), u = 2^-24.
+    partial sum of K <= 133144 of them is representable).  A sequential fp32
+    sum is within gamma_K * sum_k |x_k w_k| (gamma_K = K u / (1 - K u),
+    u = 2^-24) of it; the matrix cores' block sums are not sequential fp32
+    additions and get the bound of fp8_mfma_bound.
 """
 from __future__ import annotations
 
@@ -99,6 +100,18 @@ def fp32_sum_bound(cx, cw) -> np.ndarray:
     u = 2.0 ** -24
     gamma = K * u / (1 - K * u)
     return gamma * (np.abs(e4m3_decode(cx)) @ np.abs(e4m3_decode(cw)).T)
+
+
+def fp8_mfma_bound(cx, cw) -> np.ndarray:
+    """Accumulation error allowed for the matrix-core fp8 GEMM: the hardware
+    sums each block of 64 products inside one MFMA with a relative error (to
+    the block's sum of |products|) measured at up to 2^-16.2 on gfx950 (the
+    block sum is not a sequence of IEEE fp32 additions), and adds the blocks
+    in fp32.  Allowed: (2^-14 + ceil(K/64) * 2^-24) * sum_k |x_k w_k| -- four
+    times the measured block error plus the fp32 block accumulation."""
+    K = np.asarray(cx).shape[1]
+    rel = 2.0 ** -14 + -(-K // 64) * 2.0 ** -24
+    return rel * (np.abs(e4m3_decode(cx)) @ np.abs(e4m3_decode(cw)).T)
 
 
 def w8a8_fp8_linear_ref(x, w, bias=None) -> dict:

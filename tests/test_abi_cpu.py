@@ -47,7 +47,8 @@ def test_max_k_matches_int32_bound(w):
 A = 0x10000   # fake, 16-byte aligned, never dereferenced
 
 
-@pytest.mark.parametrize("fn", ["w8a8_quantize_weight", "w8a8_quantize_act"])
+@pytest.mark.parametrize("fn", ["w8a8_quantize_weight", "w8a8_quantize_act",
+                                "w8a8_quantize_weight_fp8", "w8a8_quantize_act_fp8"])
 def test_quantize_validation(w, fn):
     f = getattr(w.lib, fn)
     assert f(None, 4, 64, A, A, None) == 1
@@ -62,7 +63,7 @@ def test_quantize_validation(w, fn):
     assert f(None, 0, 64, None, None, None) == 0
 
 
-@pytest.mark.parametrize("fn", ["w8a8_linear", "w8a8_linear_gelu"])
+@pytest.mark.parametrize("fn", ["w8a8_linear", "w8a8_linear_gelu", "w8a8_linear_fp8"])
 def test_linear_validation(w, fn):
     L = getattr(w.lib, fn)
     args = lambda **k: [k.get(n, A) for n in ("xq", "sx", "wq", "sw", "b", "y")] + \
@@ -86,14 +87,16 @@ def test_linear_validation(w, fn):
     assert w.lib.w8a8_linear_tile(*args(M=0)[:-1], w.num_tiles(), None) == 5
 
 
-def test_gemm_i32_validation(w):
-    G = w.lib.w8a8_gemm_i32
+@pytest.mark.parametrize("fn", ["w8a8_gemm_i32", "w8a8_gemm_f32_fp8"])
+def test_gemm_raw_validation(w, fn):
+    G = getattr(w.lib, fn)
     assert G(None, A, A, 8, 8, 64, None) == 1
     assert G(A, A, None, 8, 8, 64, None) == 1
     assert G(A, A, A, 8, 8, 133144 + 16, None) == 2
     assert G(A, A, A + 2, 8, 8, 64, None) == 3
     assert G(A, A, A, 0, 8, 133136, None) == 0
-    assert w.lib.w8a8_gemm_i32_tile(A, A, A, 0, 8, 64, -7, None) == 0   # negative = automatic
+    assert getattr(w.lib, fn + "_tile")(A, A, A, 0, 8, 64, -7, None) == 0   # negative = automatic
+    assert getattr(w.lib, fn + "_tile")(A, A, A, 0, 8, 64, 99, None) == 5
 
 
 def test_tile_table(w):

@@ -8,10 +8,12 @@ Ideogram 4.0" (arXiv 2606.14598).
 """
 from ._lib import LIB_PATH, MAX_K, W8A8Error, lib, status_str
 from .module import W8A8Linear
-from .ops import (dequantize_rows, gemm_i32, linear, num_tiles, quantize_act, quantize_weight,
+from .ops import (dequantize_rows, gemm_f32_fp8, gemm_i32, linear, linear_fp8, num_tiles,
+                  quantize_act, quantize_act_fp8, quantize_weight, quantize_weight_fp8,
                   select_tile, tile_info)
 from .slowpath import dequant_bf16_linear
 
 __all__ = ["LIB_PATH", "MAX_K", "W8A8Error", "W8A8Linear", "dequant_bf16_linear",
-           "dequantize_rows", "gemm_i32", "lib", "linear", "num_tiles", "quantize_act",
-           "quantize_weight", "select_tile", "status_str", "tile_info"]
+           "dequantize_rows", "gemm_f32_fp8", "gemm_i32", "lib", "linear", "linear_fp8",
+           "num_tiles", "quantize_act", "quantize_act_fp8", "quantize_weight",
+           "quantize_weight_fp8", "select_tile", "status_str", "tile_info"]

@@ -39,6 +39,12 @@ def _load() -> ctypes.CDLL:
         "w8a8_linear_tile": (st, [p, p, p, p, p, p, i64, i64, i64, i32, p]),
         "w8a8_gemm_i32_tile": (st, [p, p, p, i64, i64, i64, i32, p]),
         "w8a8_linear_gelu": (st, [p, p, p, p, p, p, i64, i64, i64, p]),
+        "w8a8_quantize_weight_fp8": (st, [p, i64, i64, p, p, p]),
+        "w8a8_quantize_act_fp8": (st, [p, i64, i64, p, p, p]),
+        "w8a8_linear_fp8": (st, [p, p, p, p, p, p, i64, i64, i64, p]),
+        "w8a8_linear_fp8_tile": (st, [p, p, p, p, p, p, i64, i64, i64, i32, p]),
+        "w8a8_gemm_f32_fp8": (st, [p, p, p, i64, i64, i64, p]),
+        "w8a8_gemm_f32_fp8_tile": (st, [p, p, p, i64, i64, i64, i32, p]),
         "w8a8_linear_gelu_tile": (st, [p, p, p, p, p, p, i64, i64, i64, i32, p]),
     }
     for name, (res, args) in sig.items():

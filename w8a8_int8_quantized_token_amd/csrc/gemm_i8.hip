@@ -43,7 +43,9 @@ namespace w8a8 {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -73,7 +75,6 @@ struct Tile {
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int TM = BM / WM, TN = BN / WN;   // per-wavefront extent
   static constexpr int FM = TM / 32, FN = TN / 32;   // 32x32 MFMA tiles per wavefront
-  static constexpr int KSUB = BK / 32;               // MFMA K steps per stage
   static constexpr int CPR = BK / 16;                // 16-byte chunks per LDS row
   static constexpr int kDmaRows = kDmaBytes / BK;    // rows moved by one wavefront DMA
   static constexpr int DX = BM / kDmaRows / kWaves;  // X DMAs per wavefront per stage
@@ -118,9 +119,10 @@ __device__ __forceinline__ float bf16_to_float(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
 }
 
-// y = fl32(fl32(fl32(float(acc) * sa) * sw) + b), each step rounded on its own.
-__device__ __forceinline__ float dequant(int acc, float sa, float sw, float b) {
-  return __fadd_rn(__fmul_rn(__fmul_rn((float)acc, sa), sw), b);
+// y = fl32(fl32(fl32(acc) * sa) * sw) + b), each step rounded on its own
+// (the int32 accumulator is converted to fp32 with round to nearest even).
+__device__ __forceinline__ float dequant(float acc, float sa, float sw, float b) {
+  return __fadd_rn(__fmul_rn(__fmul_rn(acc, sa), sw), b);
 }
 
 // GELU with the exact (erf) definition, gelu(v) = v * Phi(v), where the
@@ -166,6 +168,25 @@ __device__ __forceinline__ void barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Operand types.  int8: v_mfma_i32_32x32x32_i8, 16 K bytes per lane and
+// step, int32 accumulators.  fp8 (e4m3): v_mfma_f32_32x32x64_f8f6f4 (the
+// scaled form with unit E8M0 scales, 127), 32 K bytes per lane and step,
+// fp32 accumulators.  Both take the lane's row of A and of B at the same K
+// positions, so any fixed assignment of K bytes to (lane half, byte) that is
+// the same for both operands gives the same dot products.
+struct OpI8 {
+  static constexpr bool kF8 = false;
+  static constexpr int kStepK = 32;   // K bytes per MFMA
+  typedef v4i Frag;
+  typedef v16i Acc;
+};
+struct OpF8 {
+  static constexpr bool kF8 = true;
+  static constexpr int kStepK = 64;
+  typedef v8i Frag;
+  typedef v16f Acc;
+};
+
 // Output tile `t` (0 <= t < tiles_m * tiles_n) -> (first row, first channel).
 // Tiles are spread so that each XCD works on a contiguous range, walked in
 // groups of kGroupM tile rows (tiles resident on one XCD share X and W panels
@@ -188,7 +209,7 @@ __device__ __forceinline__ void tile_origin(int t, int tiles_m, int tiles_n, int
 // output tiles t = blockIdx.x, blockIdx.x + gridDim.x, ...  With the split
 // ring, the first two requests of a workgroup's next tile are issued before
 // the epilogue of the current one, so the epilogue hides their latency.
-template <class T, Epilogue EPI>
+template <class T, Epilogue EPI, class Op>
 __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     const int8_t* __restrict__ X, const int8_t* __restrict__ W, const float* __restrict__ sx,
     const float* __restrict__ sw, const uint16_t* __restrict__ bias, void* __restrict__ out,
@@ -264,43 +285,74 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     issue_w(a, buf + T::BM * T::BK, kt);
   };
 
-  v16i acc[T::FM][T::FN];
+  constexpr int KSUB = T::BK / Op::kStepK;   // MFMA K steps per stage
+  constexpr int CPS = Op::kStepK / 32;        // 16-byte chunks per lane and K step
+  static_assert(KSUB >= 1, "a stage holds at least one MFMA K step");
+  typename Op::Acc acc[T::FM][T::FN];
 
-  // Fragment registers, double buffered by MFMA K step parity.
-  v4i fa[2][T::FN], fb[2][T::FM];
+  // Fragment registers, double buffered by MFMA K step parity (int8); the
+  // fp8 fragments are twice as wide and single buffered, which keeps the
+  // 128 accumulators and both operands within 256 VGPRs.  In K step s lane
+  // half h reads chunks (2s + h)*CPS ... + CPS-1 of its row.
+  constexpr int NB = Op::kF8 ? 1 : 2;
+  typename Op::Frag fa[NB][T::FN], fb[NB][T::FM];
+  auto read_frag = [&](const int8_t* base, int r, int c) {
+    typename Op::Frag f;
+    if constexpr (CPS == 1) {
+      f = *reinterpret_cast<const v4i*>(base + r * T::BK + swz<T::CPR>(r, c) * 16);
+    } else {
+      const v4i lo = *reinterpret_cast<const v4i*>(base + r * T::BK + swz<T::CPR>(r, c) * 16);
+      const v4i hi = *reinterpret_cast<const v4i*>(base + r * T::BK + swz<T::CPR>(r, c + 1) * 16);
+      f = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    return f;
+  };
   auto frag2 = [&](const int8_t* xs, const int8_t* ws, int s, int slot) {
-    const int c = s * 2 + khalf;
+    slot %= NB;
+    const int c = (s * 2 + khalf) * CPS;
 #pragma unroll
-    for (int j = 0; j < T::FN; ++j) {
-      const int r = wn * T::TN + j * 32 + row_in;
-      fa[slot][j] = *reinterpret_cast<const v4i*>(ws + r * T::BK + swz<T::CPR>(r, c) * 16);
-    }
+    for (int j = 0; j < T::FN; ++j) fa[slot][j] = read_frag(ws, wn * T::TN + j * 32 + row_in, c);
 #pragma unroll
-    for (int i = 0; i < T::FM; ++i) {
-      const int r = wm * T::TM + i * 32 + row_in;
-      fb[slot][i] = *reinterpret_cast<const v4i*>(xs + r * T::BK + swz<T::CPR>(r, c) * 16);
-    }
+    for (int i = 0; i < T::FM; ++i) fb[slot][i] = read_frag(xs, wm * T::TM + i * 32 + row_in, c);
   };
   auto frag = [&](const int8_t* buf, int s, int slot) { frag2(buf, buf + T::BM * T::BK, s, slot); };
   auto mfmas = [&](int slot) {
+    slot %= NB;
 #pragma unroll
     for (int i = 0; i < T::FM; ++i)
 #pragma unroll
-      for (int j = 0; j < T::FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[slot][j], fb[slot][i], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < T::FN; ++j) {
+        if constexpr (Op::kF8)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fa[slot][j], fb[slot][i], acc[i][j], 0, 0, 0, 127, 0, 127);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[slot][j], fb[slot][i], acc[i][j], 0, 0, 0);
+      }
   };
 
   // Scheduling of the code after a barrier: the next stage's first fragment
   // reads, then the last K step's MFMAs each followed by one stage request
   // (and its address arithmetic), so the MFMA pipe restarts right away.
   auto interleave = [&]() {
-    __builtin_amdgcn_sched_group_barrier(0x100, T::FM + T::FN, 0);   // fragment reads
+    __builtin_amdgcn_sched_group_barrier(0x100, (T::FM + T::FN) * CPS, 0);   // fragment reads
 #pragma unroll
     for (int q = 0; q < T::FM * T::FN; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);             // address VALU
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);             // one DMA
     }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Single-buffered fragments: the MFMAs of a K step go before the reads of
+  // the next step's fragments into the same registers.
+  auto interleave1 = [&]() {
+#pragma unroll
+    for (int q = 0; q < T::FM * T::FN; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);             // address VALU
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);             // one DMA
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, (T::FM + T::FN) * CPS, 0);   // fragment reads
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -310,8 +362,25 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
   // start reading stage k+1's first fragments under the MFMAs of the last K
   // step.  A stage is thus requested a full S-1 steps before it is needed.
   auto step = [&](const TileAddr& a, int8_t* cur, int8_t* nxt, int k) {
+    if constexpr (NB == 1) {
 #pragma unroll
-    for (int s = 0; s + 1 < T::KSUB; ++s) {
+      for (int s = 0; s + 1 < KSUB; ++s) {
+        mfmas(0);
+        __builtin_amdgcn_sched_barrier(0);
+        frag(cur, s + 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      wait_lgkmcnt0();
+      wait_vmcnt<(T::S - 2) * T::D>();
+      barrier();
+      issue(a, cur, k + T::S);
+      mfmas(0);
+      frag(nxt, 0, 0);
+      interleave1();
+      return;
+    }
+#pragma unroll
+    for (int s = 0; s + 1 < KSUB; ++s) {
       frag(cur, s + 1, (s + 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
       mfmas(s & 1);
@@ -320,9 +389,9 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     wait_lgkmcnt0();                 // this wavefront's reads of `cur` are done
     wait_vmcnt<(T::S - 2) * T::D>();  // its DMAs of stage k+1 have landed
     barrier();                       // ... and everyone's
-    frag(nxt, 0, T::KSUB & 1);
+    frag(nxt, 0, KSUB & 1);
     issue(a, cur, k + T::S);
-    mfmas((T::KSUB - 1) & 1);
+    mfmas((KSUB - 1) & 1);
     interleave();
   };
 
@@ -333,8 +402,26 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
   // X has two steps to land.
   auto step_split = [&](const TileAddr& a, int8_t* xc, int8_t* wc, int8_t* xn, int8_t* wn1,
                         int k) {
+    if constexpr (NB == 1) {
 #pragma unroll
-    for (int s = 0; s + 1 < T::KSUB; ++s) {
+      for (int s = 0; s + 1 < KSUB; ++s) {
+        mfmas(0);
+        __builtin_amdgcn_sched_barrier(0);
+        frag2(xc, wc, s + 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      wait_lgkmcnt0();
+      wait_vmcnt<T::DX>();
+      barrier();
+      issue_w(a, wc, k + 2);
+      issue_x(a, xc, k + 3);
+      mfmas(0);
+      frag2(xn, wn1, 0, 0);
+      interleave1();
+      return;
+    }
+#pragma unroll
+    for (int s = 0; s + 1 < KSUB; ++s) {
       frag2(xc, wc, s + 1, (s + 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
       mfmas(s & 1);
@@ -343,10 +430,10 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     wait_lgkmcnt0();
     wait_vmcnt<T::DX>();   // everything but X_{k+2} (the last request) has landed
     barrier();
-    frag2(xn, wn1, 0, T::KSUB & 1);
+    frag2(xn, wn1, 0, KSUB & 1);
     issue_w(a, wc, k + 2);
     issue_x(a, xc, k + 3);
-    mfmas((T::KSUB - 1) & 1);
+    mfmas((KSUB - 1) & 1);
     interleave();
   };
 
@@ -400,7 +487,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
 #pragma unroll
     for (int i = 0; i < T::FM; ++i)
 #pragma unroll
-      for (int j = 0; j < T::FN; ++j) acc[i][j] = v16i{};
+      for (int j = 0; j < T::FN; ++j) acc[i][j] = typename Op::Acc{};
 
     // ---- K loop ----
     if constexpr (T::kSplit) {
@@ -507,10 +594,10 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
         for (int i = 0; i < T::FM; ++i) {
           // 4 bf16 outputs (two packed words) of run g: channels nj + 8g + 4*khalf + 0..3
           uint32_t w[4][2];
-          const v16i& c = acc[i][j];
+          const typename Op::Acc& c = acc[i][j];
           // the fp32 output value (GELU applied for the gelu epilogue)
           auto val = [&](int e, float s_w, float b) {
-            const float y = dequant(c[e], sa[i], s_w, b);
+            const float y = dequant((float)c[e], sa[i], s_w, b);
             if constexpr (EPI == Epilogue::kBf16GeluScaleBias) return gelu(y);
             else return y;
           };
@@ -580,13 +667,19 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int n = n0 + wn * T::TN + j * 32 + g * 8 + khalf * 4;
+            // raw accumulators (fp8: the fp32 bits).  The whole vector is
+            // reinterpreted: bit-casting single fp32 elements of the fp8 MFMA's
+            // result miscompiles (every element is taken to equal element 0).
+            const v16i av = __builtin_bit_cast(v16i, acc[i][j]);
+            int32_t a4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a4[e] = av[g * 4 + e];
             if (vec_store && n + 3 < N) {
-              *reinterpret_cast<v4i*>(crow + n) =
-                  v4i{acc[i][j][g * 4], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]};
+              *reinterpret_cast<v4i*>(crow + n) = v4i{a4[0], a4[1], a4[2], a4[3]};
             } else {
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                if (n + e < N) crow[n + e] = acc[i][j][g * 4 + e];
+                if (n + e < N) crow[n + e] = a4[e];
             }
           }
         }
@@ -623,7 +716,7 @@ int num_cus() {
 
 // Launch tile configuration T on the sub-problem M x N x K whose output rows
 // are `ldy` elements apart.
-template <class T>
+template <class T, class Op>
 hipError_t launch_t(Epilogue epi, const int8_t* xq, const int8_t* wq, const float* sx,
                     const float* sw, const uint16_t* bias, void* out, int64_t M, int64_t N,
                     int64_t K, int64_t ldy, hipStream_t stream) {
@@ -636,17 +729,17 @@ hipError_t launch_t(Epilogue epi, const int8_t* xq, const int8_t* wq, const floa
   const uintptr_t o = reinterpret_cast<uintptr_t>(out);
   if (epi == Epilogue::kBf16ScaleBias) {
     const int vec = (ldy % 8 == 0) && (o % 16 == 0);
-    hipLaunchKernelGGL((gemm_i8_kernel<T, Epilogue::kBf16ScaleBias>), grid, block, 0, stream, xq,
+    hipLaunchKernelGGL((gemm_i8_kernel<T, Epilogue::kBf16ScaleBias, Op>), grid, block, 0, stream, xq,
                        wq, sx, sw, bias, out, (int)M, (int)N, (int)K, (int)ldy, tiles_m, tiles_n,
                        vec);
   } else if (epi == Epilogue::kBf16GeluScaleBias) {
     const int vec = (ldy % 8 == 0) && (o % 16 == 0);
-    hipLaunchKernelGGL((gemm_i8_kernel<T, Epilogue::kBf16GeluScaleBias>), grid, block, 0, stream,
+    hipLaunchKernelGGL((gemm_i8_kernel<T, Epilogue::kBf16GeluScaleBias, Op>), grid, block, 0, stream,
                        xq, wq, sx, sw, bias, out, (int)M, (int)N, (int)K, (int)ldy, tiles_m,
                        tiles_n, vec);
   } else {
     const int vec = (ldy % 4 == 0) && (o % 16 == 0);
-    hipLaunchKernelGGL((gemm_i8_kernel<T, Epilogue::kRawI32>), grid, block, 0, stream, xq, wq,
+    hipLaunchKernelGGL((gemm_i8_kernel<T, Epilogue::kRawI32, Op>), grid, block, 0, stream, xq, wq,
                        nullptr, nullptr, nullptr, out, (int)M, (int)N, (int)K, (int)ldy, tiles_m,
                        tiles_n, vec);
   }
@@ -670,17 +763,18 @@ const TileDesc kCfgs[kNumCfg] = {desc<CfgSplit>(), desc<CfgWhole>(), desc<Cfg192
                                  desc<CfgTail>(), desc<Cfg256x128>(), desc<Cfg128>(),
                                  desc<Cfg64>()};
 
+template <class Op>
 hipError_t launch_cfg(int cfg, Epilogue epi, const int8_t* xq, const int8_t* wq, const float* sx,
                       const float* sw, const uint16_t* bias, void* out, int64_t M, int64_t N,
                       int64_t K, int64_t ldy, hipStream_t s) {
   switch (cfg) {
-    case kSplit256: return launch_t<CfgSplit>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
-    case kWhole256: return launch_t<CfgWhole>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
-    case k192: return launch_t<Cfg192>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
-    case kTail128x256: return launch_t<CfgTail>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
-    case k256x128: return launch_t<Cfg256x128>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
-    case k128: return launch_t<Cfg128>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
-    case k64: return launch_t<Cfg64>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
+    case kSplit256: return launch_t<CfgSplit, Op>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
+    case kWhole256: return launch_t<CfgWhole, Op>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
+    case k192: return launch_t<Cfg192, Op>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
+    case kTail128x256: return launch_t<CfgTail, Op>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
+    case k256x128: return launch_t<Cfg256x128, Op>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
+    case k128: return launch_t<Cfg128, Op>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
+    case k64: return launch_t<Cfg64, Op>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -781,20 +875,34 @@ int select_tile(int64_t M, int64_t N, int64_t K) {
   return best;
 }
 
-hipError_t launch_gemm(int tile, Epilogue epi, const int8_t* xq, const int8_t* wq,
+template <class Op>
+hipError_t launch_plan(int tile, Epilogue epi, const int8_t* xq, const int8_t* wq,
                        const float* sx, const float* sw, const uint16_t* bias, void* out,
                        int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   if (tile < 0 || tile >= kNumPlans) return hipErrorInvalidValue;
   const Plan& p = kPlans[tile];
   const int64_t c = p.tail >= 0 ? main_columns(kCfgs[p.main], M, N) : 0;
-  if (c == 0) return launch_cfg(p.main, epi, xq, wq, sx, sw, bias, out, M, N, K, N, stream);
+  if (c == 0) return launch_cfg<Op>(p.main, epi, xq, wq, sx, sw, bias, out, M, N, K, N, stream);
   const int64_t nm = c * kCfgs[p.main].block_n;   // channels done by the main tiles
-  hipError_t e = launch_cfg(p.main, epi, xq, wq, sx, sw, bias, out, M, nm, K, N, stream);
+  hipError_t e = launch_cfg<Op>(p.main, epi, xq, wq, sx, sw, bias, out, M, nm, K, N, stream);
   if (e != hipSuccess) return e;
   const size_t esz = epi == Epilogue::kRawI32 ? 4 : 2;
   void* out_tail = static_cast<char*>(out) + nm * esz;
-  return launch_cfg(p.tail, epi, xq, wq + nm * K, sx, sw ? sw + nm : nullptr,
-                    bias ? bias + nm : nullptr, out_tail, M, N - nm, K, N, stream);
+  return launch_cfg<Op>(p.tail, epi, xq, wq + nm * K, sx, sw ? sw + nm : nullptr,
+                        bias ? bias + nm : nullptr, out_tail, M, N - nm, K, N, stream);
+}
+
+hipError_t launch_gemm(int tile, Epilogue epi, const int8_t* xq, const int8_t* wq,
+                       const float* sx, const float* sw, const uint16_t* bias, void* out,
+                       int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  return launch_plan<OpI8>(tile, epi, xq, wq, sx, sw, bias, out, M, N, K, stream);
+}
+
+hipError_t launch_gemm_fp8(int tile, Epilogue epi, const uint8_t* xq, const uint8_t* wq,
+                           const float* sx, const float* sw, const uint16_t* bias, void* out,
+                           int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  return launch_plan<OpF8>(tile, epi, reinterpret_cast<const int8_t*>(xq),
+                           reinterpret_cast<const int8_t*>(wq), sx, sw, bias, out, M, N, K, stream);
 }
 
 }  // namespace w8a8

@@ -12,6 +12,10 @@ namespace w8a8 {
 hipError_t launch_quantize_rows(const uint16_t* x, int8_t* q, float* scale,
                                 int64_t R, int64_t K, hipStream_t stream);
 
+// The same with e4m3 codes: scale fl32(amax/448), q = e4m3(fl32(x/scale)).
+hipError_t launch_quantize_rows_fp8(const uint16_t* x, uint8_t* q, float* scale, int64_t R,
+                                    int64_t K, hipStream_t stream);
+
 // Row-wise dequantization: out[r,k] = bf16(fl32(float(q[r,k]) * scale[r])),
 // q int8 [R,K] -> out bf16 bits [R,K].  Requires K % 16 == 0 and R > 0.
 hipError_t launch_dequantize_rows(const int8_t* q, const float* scale, uint16_t* out, int64_t R,
@@ -39,5 +43,12 @@ enum class Epilogue { kBf16ScaleBias, kBf16GeluScaleBias, kRawI32 };
 hipError_t launch_gemm(int tile, Epilogue epi, const int8_t* xq, const int8_t* wq,
                        const float* sx, const float* sw, const uint16_t* bias, void* out,
                        int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// The fp8 (e4m3) variant: the same tiles and epilogues on
+// v_mfma_f32_32x32x64_f8f6f4; for kRawI32 `out` receives the fp32
+// accumulators' bits.
+hipError_t launch_gemm_fp8(int tile, Epilogue epi, const uint8_t* xq, const uint8_t* wq,
+                           const float* sx, const float* sw, const uint16_t* bias, void* out,
+                           int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 }  // namespace w8a8

@@ -72,6 +72,20 @@ w8a8_status w8a8_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* x
   return quantize(x, M, K, xq, x_scale, stream);
 }
 
+w8a8_status w8a8_quantize_weight_fp8(const uint16_t* w, int64_t N, int64_t K, uint8_t* wq,
+                                     float* w_scale, hipStream_t stream) {
+  const w8a8_status st = check_quant(w, N, K, reinterpret_cast<int8_t*>(wq), w_scale);
+  if (st != W8A8_OK || N == 0) return st;
+  return w8a8::launch_quantize_rows_fp8(w, wq, w_scale, N, K, stream) == hipSuccess
+             ? W8A8_OK
+             : W8A8_ERR_LAUNCH;
+}
+
+w8a8_status w8a8_quantize_act_fp8(const uint16_t* x, int64_t M, int64_t K, uint8_t* xq,
+                                  float* x_scale, hipStream_t stream) {
+  return w8a8_quantize_weight_fp8(x, M, K, xq, x_scale, stream);
+}
+
 w8a8_status w8a8_dequantize_rows(const int8_t* q, const float* scale, int64_t R, int64_t K,
                                  uint16_t* out, hipStream_t stream) {
   if (R < 0 || R > kMaxRows || K < 16 || K % 16 != 0 || K > kMaxQuantK) return W8A8_ERR_SHAPE;
@@ -88,7 +102,8 @@ namespace {
 
 w8a8_status linear_epi(w8a8::Epilogue epi, const int8_t* xq, const float* x_scale,
                        const int8_t* wq, const float* w_scale, const uint16_t* bias, uint16_t* y,
-                       int64_t M, int64_t N, int64_t K, int tile, hipStream_t stream) {
+                       int64_t M, int64_t N, int64_t K, int tile, hipStream_t stream,
+                       bool fp8 = false) {
   w8a8_status st = check_gemm_shape(M, N, K);
   if (st != W8A8_OK) return st;
   const int t = resolve_tile(tile, M, N, K);
@@ -100,10 +115,12 @@ w8a8_status linear_epi(w8a8::Epilogue epi, const int8_t* xq, const float* x_scal
   if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(y, 2) ||
       (bias && !aligned(bias, 2)))
     return W8A8_ERR_ALIGN;
-  return w8a8::launch_gemm(t, epi, xq, wq, x_scale, w_scale, bias, y, M, N, K, stream) ==
-                 hipSuccess
-             ? W8A8_OK
-             : W8A8_ERR_LAUNCH;
+  const hipError_t e =
+      fp8 ? w8a8::launch_gemm_fp8(t, epi, reinterpret_cast<const uint8_t*>(xq),
+                                  reinterpret_cast<const uint8_t*>(wq), x_scale, w_scale, bias, y,
+                                  M, N, K, stream)
+          : w8a8::launch_gemm(t, epi, xq, wq, x_scale, w_scale, bias, y, M, N, K, stream);
+  return e == hipSuccess ? W8A8_OK : W8A8_ERR_LAUNCH;
 }
 
 }  // namespace
@@ -155,6 +172,42 @@ w8a8_status w8a8_gemm_i32_tile(const int8_t* xq, const int8_t* wq, int32_t* acc,
 w8a8_status w8a8_gemm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc, int64_t M, int64_t N,
                           int64_t K, hipStream_t stream) {
   return w8a8_gemm_i32_tile(xq, wq, acc, M, N, K, -1, stream);
+}
+
+w8a8_status w8a8_linear_fp8_tile(const uint8_t* xq, const float* x_scale, const uint8_t* wq,
+                                 const float* w_scale, const uint16_t* bias, uint16_t* y,
+                                 int64_t M, int64_t N, int64_t K, int tile, hipStream_t stream) {
+  return linear_epi(w8a8::Epilogue::kBf16ScaleBias, reinterpret_cast<const int8_t*>(xq), x_scale,
+                    reinterpret_cast<const int8_t*>(wq), w_scale, bias, y, M, N, K, tile, stream,
+                    true);
+}
+
+w8a8_status w8a8_linear_fp8(const uint8_t* xq, const float* x_scale, const uint8_t* wq,
+                            const float* w_scale, const uint16_t* bias, uint16_t* y, int64_t M,
+                            int64_t N, int64_t K, hipStream_t stream) {
+  return w8a8_linear_fp8_tile(xq, x_scale, wq, w_scale, bias, y, M, N, K, -1, stream);
+}
+
+w8a8_status w8a8_gemm_f32_fp8_tile(const uint8_t* xq, const uint8_t* wq, float* acc, int64_t M,
+                                   int64_t N, int64_t K, int tile, hipStream_t stream) {
+  w8a8_status st = check_gemm_shape(M, N, K);
+  if (st != W8A8_OK) return st;
+  const int t = resolve_tile(tile, M, N, K);
+  if (t < 0) return W8A8_ERR_ARG;
+  if (M == 0) return W8A8_OK;
+  st = check_gemm_ptrs(reinterpret_cast<const int8_t*>(xq), reinterpret_cast<const int8_t*>(wq),
+                       acc);
+  if (st != W8A8_OK) return st;
+  if (!aligned(acc, 4)) return W8A8_ERR_ALIGN;
+  return w8a8::launch_gemm_fp8(t, w8a8::Epilogue::kRawI32, xq, wq, nullptr, nullptr, nullptr, acc,
+                               M, N, K, stream) == hipSuccess
+             ? W8A8_OK
+             : W8A8_ERR_LAUNCH;
+}
+
+w8a8_status w8a8_gemm_f32_fp8(const uint8_t* xq, const uint8_t* wq, float* acc, int64_t M,
+                              int64_t N, int64_t K, hipStream_t stream) {
+  return w8a8_gemm_f32_fp8_tile(xq, wq, acc, M, N, K, -1, stream);
 }
 
 int w8a8_num_tiles(void) { return w8a8::num_tiles(); }

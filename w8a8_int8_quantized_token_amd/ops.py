@@ -30,14 +30,14 @@ def _need(t: torch.Tensor, dtype, ndim: int, name: str) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
-def _quant(fn, x: torch.Tensor, q=None, s=None, name="x"):
+def _quant(fn, x: torch.Tensor, q=None, s=None, name="x", code_dtype=torch.int8):
     _need(x, torch.bfloat16, 2, name)
     R, K = x.shape
     if q is None:
-        q = torch.empty((R, K), dtype=torch.int8, device=x.device)
+        q = torch.empty((R, K), dtype=code_dtype, device=x.device)
     if s is None:
         s = torch.empty((R,), dtype=torch.float32, device=x.device)
-    _need(q, torch.int8, 2, "q")
+    _need(q, code_dtype, 2, "q")
     _need(s, torch.float32, 1, "scale")
     if tuple(q.shape) != (R, K) or s.shape[0] != R:
         raise ValueError("output shapes do not match the input")
@@ -72,9 +72,19 @@ def dequantize_rows(q: torch.Tensor, scale: torch.Tensor, out=None):
     return out
 
 
-def _gemm_args(xq, wq):
-    _need(xq, torch.int8, 2, "xq")
-    _need(wq, torch.int8, 2, "wq")
+def quantize_weight_fp8(w: torch.Tensor, wq=None, w_scale=None):
+    """w bf16 [N,K] -> (e4m3 codes uint8 [N,K], w_scale fp32 [N]), per output channel."""
+    return _quant(lib.w8a8_quantize_weight_fp8, w, wq, w_scale, "w", torch.uint8)
+
+
+def quantize_act_fp8(x: torch.Tensor, xq=None, x_scale=None):
+    """x bf16 [M,K] -> (e4m3 codes uint8 [M,K], x_scale fp32 [M]), per token."""
+    return _quant(lib.w8a8_quantize_act_fp8, x, xq, x_scale, "x", torch.uint8)
+
+
+def _gemm_args(xq, wq, code_dtype=torch.int8):
+    _need(xq, code_dtype, 2, "xq")
+    _need(wq, code_dtype, 2, "wq")
     M, K = xq.shape
     N, K2 = wq.shape
     if K != K2:
@@ -117,6 +127,43 @@ def gemm_i32(xq, wq, acc=None, tile: int = -1):
         raise ValueError("acc shape does not match [M,N]")
     check(lib.w8a8_gemm_i32_tile(xq.data_ptr(), wq.data_ptr(), acc.data_ptr(), M, N, K, tile,
                                  _stream(xq)), "w8a8_gemm_i32")
+    return acc
+
+
+def linear_fp8(xq, x_scale, wq, w_scale, bias=None, y=None, tile: int = -1):
+    """The fp8 variant: e4m3 codes (uint8) -> bf16 y [M,N] = dequant(xq @ wq^T) + bias."""
+    M, N, K = _gemm_args(xq, wq, torch.uint8)
+    _need(x_scale, torch.float32, 1, "x_scale")
+    _need(w_scale, torch.float32, 1, "w_scale")
+    if x_scale.shape[0] != M or w_scale.shape[0] != N:
+        raise ValueError("scale lengths do not match M / N")
+    bptr = None
+    if bias is not None:
+        _need(bias, torch.bfloat16, 1, "bias")
+        if bias.shape[0] != N:
+            raise ValueError("bias length does not match N")
+        bptr = bias.data_ptr()
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    _need(y, torch.bfloat16, 2, "y")
+    if tuple(y.shape) != (M, N):
+        raise ValueError("y shape does not match [M,N]")
+    check(lib.w8a8_linear_fp8_tile(xq.data_ptr(), x_scale.data_ptr(), wq.data_ptr(),
+                                   w_scale.data_ptr(), bptr, y.data_ptr(), M, N, K, tile,
+                                   _stream(xq)), "w8a8_linear_fp8")
+    return y
+
+
+def gemm_f32_fp8(xq, wq, acc=None, tile: int = -1):
+    """fp32 accumulators acc [M,N] = xq @ wq^T of e4m3 codes (diagnostic)."""
+    M, N, K = _gemm_args(xq, wq, torch.uint8)
+    if acc is None:
+        acc = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    _need(acc, torch.float32, 2, "acc")
+    if tuple(acc.shape) != (M, N):
+        raise ValueError("acc shape does not match [M,N]")
+    check(lib.w8a8_gemm_f32_fp8_tile(xq.data_ptr(), wq.data_ptr(), acc.data_ptr(), M, N, K, tile,
+                                     _stream(xq)), "w8a8_gemm_f32_fp8")
     return acc
 
 
