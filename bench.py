@@ -54,6 +54,9 @@ def parse():
     p.add_argument("--cpu-rows", type=int, default=4096, help="tokens per linear in the CPU sample")
     p.add_argument("--no-cold", action="store_true", help="skip the cold-cache GEMM / quantize timings")
     p.add_argument("--no-other", action="store_true", help="skip timing the other workloads' linears")
+    p.add_argument("--only-step", action="store_true",
+                   help="time the step only: no comparators, variants, cold or other workloads "
+                        "(for profiler runs, whose GEMM dispatches must be the step's alone)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run a plain 1 GiB streaming copy 3 times (the reference kernel "
                         "for scaling HBM byte counters)")
@@ -226,6 +229,66 @@ def time_fp8_variant(w8, layers, stream, iters: int = 10) -> dict:
                     "MI355X dense fp8 peak = int8 peak = 5.0 P"}
 
 
+def median_ms(fn, stream, n):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(n):
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return float(np.median(ts))
+
+
+def bf16_comparator(layers, per, stream, steps) -> float:
+    """torch F.linear (hipBLASLt bf16) on the same shapes: median per linear."""
+    for L in layers:
+        torch.nn.functional.linear(L["x"], L["wbf"], L["b"])
+    torch.cuda.synchronize()
+    total = 0.0
+    for p, L in zip(per, layers):
+        t = median_ms(lambda: torch.nn.functional.linear(L["x"], L["wbf"], L["b"]), stream, max(3, steps // 2))
+        p["bf16_us"] = round(t * 1e3, 2)
+        total += t
+    return total
+
+
+def cold_timings(w8, layers, per, stream, dev, step_ops, q_bytes) -> dict:
+    log("cold-cache timings")
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    g_sum = q_sum = 0.0
+    for p, L in zip(per, layers):
+        s = L["shape"]
+        g = time_cold(lambda: w8.linear(L["xq"], L["xs"], L["wq"], L["ws"], L["b"], y=L["y"]), stream, scrub)
+        q = time_cold(lambda: w8.quantize_act(L["x"], L["xq"], L["xs"]), stream, scrub)
+        p["gemm_cold_us"] = round(g * 1e3, 2)
+        p["quant_cold_us"] = round(q * 1e3, 2)
+        p["quant_cold_gbs"] = round((3 * s.M * s.K + 4 * s.M) / q / 1e6, 1)
+        g_sum += g
+        q_sum += q
+    del scrub
+    return {"gemm_tops": round(step_ops / g_sum / 1e9, 1),
+            "linear_tops": round(step_ops / (g_sum + q_sum) / 1e9, 1),
+            "quant_gbs": round(q_bytes / q_sum / 1e6, 1),
+            "note": "median of 5 runs per launch, 512 MB cache scrub before each"}
+
+
+def slow_path(w8, layers, per, stream, steps) -> float:
+    """The same linears through quantize -> dequantize to bf16 -> bf16 GEMM."""
+    total = 0.0
+    for p, L in zip(per, layers):
+        scratch = {}
+        fn = lambda: w8.dequant_bf16_linear(L["x"], L["wq"], L["ws"], L["b"], scratch)
+        fn()
+        torch.cuda.synchronize()
+        t = median_ms(fn, stream, max(3, steps // 2))
+        p["dequant_bf16_us"] = round(t * 1e3, 2)
+        total += t
+        del scratch
+    return total
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -307,74 +370,31 @@ def main():
     q_bytes = sum(3 * L["shape"].M * L["shape"].K + 4 * L["shape"].M for L in layers)
     q_total_ms = float(q_ms.mean(axis=0).sum())
 
+    extras = not args.only_step
     # ---- bf16 comparator: torch F.linear, same shapes, same GPU ----
-    log("bf16 comparator")
-    for L in layers:
-        torch.nn.functional.linear(L["x"], L["wbf"], L["b"])
-    torch.cuda.synchronize()
-    bf_ms = []
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for L in layers:
-        ts = []
-        for _ in range(max(3, args.steps // 2)):
-            e0.record(stream)
-            torch.nn.functional.linear(L["x"], L["wbf"], L["b"])
-            e1.record(stream)
-            e1.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        bf_ms.append(float(np.median(ts)))
-    bf_total = sum(bf_ms)
-    for p, t in zip(per, bf_ms):
-        p["bf16_us"] = round(t * 1e3, 2)
+    bf_total = None
+    if extras:
+        log("bf16 comparator")
+        bf_total = bf16_comparator(layers, per, stream, args.steps)
 
     # ---- cold caches: GEMM and quantize with L2 and Infinity Cache flushed ----
     cold = None
-    if not args.no_cold:
-        log("cold-cache timings")
-        scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        cold = {}
-        for i, L in enumerate(layers):
-            s = L["shape"]
-            g = time_cold(lambda: w8.linear(L["xq"], L["xs"], L["wq"], L["ws"], L["b"], y=L["y"]), stream, scrub)
-            q = time_cold(lambda: w8.quantize_act(L["x"], L["xq"], L["xs"]), stream, scrub)
-            per[i]["gemm_cold_us"] = round(g * 1e3, 2)
-            per[i]["quant_cold_us"] = round(q * 1e3, 2)
-            per[i]["quant_cold_gbs"] = round((3 * s.M * s.K + 4 * s.M) / q / 1e6, 1)
-            cold[s.name] = (g, q)
-        del scrub
-        g_sum = sum(v[0] for v in cold.values())
-        q_sum = sum(v[1] for v in cold.values())
-        cold = {"gemm_tops": round(step_ops / g_sum / 1e9, 1),
-                "linear_tops": round(step_ops / (g_sum + q_sum) / 1e9, 1),
-                "quant_gbs": round(q_bytes / q_sum / 1e6, 1),
-                "note": "median of 5 runs per launch, 512 MB cache scrub before each"}
+    if extras and not args.no_cold:
+        cold = cold_timings(w8, layers, per, stream, dev, step_ops, q_bytes)
 
     # ---- the dequantize-to-bf16 path the method replaces (same int8 weights) ----
-    log("dequantize-to-bf16 comparator")
-    slow_ms = []
-    for L in layers:
-        scratch = {}
-        fn = lambda: w8.dequant_bf16_linear(L["x"], L["wq"], L["ws"], L["b"], scratch)
-        fn()
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(max(3, args.steps // 2)):
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            e1.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        slow_ms.append(float(np.median(ts)))
-        del scratch
-    slow_total = sum(slow_ms)
-    for p, t in zip(per, slow_ms):
-        p["dequant_bf16_us"] = round(t * 1e3, 2)
+    slow_total = None
+    if extras:
+        log("dequantize-to-bf16 comparator")
+        slow_total = slow_path(w8, layers, per, stream, args.steps)
 
-    log("fp8 variant")
-    fp8 = time_fp8_variant(w8, layers, stream)
+    fp8 = None
+    if extras:
+        log("fp8 variant")
+        fp8 = time_fp8_variant(w8, layers, stream)
 
     other = None
-    if not args.no_other:
+    if extras and not args.no_other:
         log("other workloads")
         other = time_other_workloads(w8, dev, stream)
 
@@ -414,12 +434,14 @@ def main():
         "cold": cold,
         "other_workloads": other,
         "fp8_variant": fp8,
-        "vs_dequant_bf16_path": {"tops": round(step_ops / slow_total / 1e9, 1),
-                                 "speedup_full_linear": round(slow_total / (gemm_total_ms + q_total_ms), 3),
-                                 "path": "quantize_act + dequantize X and W to bf16 + torch F.linear"},
-        "vs_bf16": {"bf16_torch_linear_tops": round(step_ops / bf_total / 1e9, 1),
-                    "speedup_full_linear": round(bf_total / (gemm_total_ms + q_total_ms), 3),
-                    "speedup_gemm_only": round(bf_total / gemm_total_ms, 3)},
+        "vs_dequant_bf16_path": None if slow_total is None else {
+            "tops": round(step_ops / slow_total / 1e9, 1),
+            "speedup_full_linear": round(slow_total / (gemm_total_ms + q_total_ms), 3),
+            "path": "quantize_act + dequantize X and W to bf16 + torch F.linear"},
+        "vs_bf16": None if bf_total is None else {
+            "bf16_torch_linear_tops": round(step_ops / bf_total / 1e9, 1),
+            "speedup_full_linear": round(bf_total / (gemm_total_ms + q_total_ms), 3),
+            "speedup_gemm_only": round(bf_total / gemm_total_ms, 3)},
         "per_linear": per,
     }
     if not args.no_cpu:
