@@ -38,6 +38,7 @@
 #include "kernels.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace w8a8 {
 namespace {
@@ -111,8 +112,9 @@ __device__ __forceinline__ int swz(int r, int c) {
 // One wavefront DMA of 16 bytes per lane from a raw buffer into LDS.  (Kept
 // out of the kernel's lambdas: called from a lambda directly, the builtin
 // keeps the host pass from emitting the kernel's launch stub.)
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, int8_t* lds, uint32_t voffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, (int)voffset, 0, 0, 0);
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, int8_t* lds, uint32_t voffset,
+                                      int soffset = 0) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, (int)voffset, soffset, 0, 0);
 }
 
 __device__ __forceinline__ float bf16_to_float(uint16_t b) {
@@ -263,27 +265,41 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
   };
   // Request the X (W) part of stage kt of tile `a` into `buf`; chunks at or
   // past K read as zeros.
-  auto issue_x = [&](const TileAddr& a, int8_t* buf, int kt) {
+  // `interior` (a std::bool_constant): the stage lies entirely inside K.
+  // Then its K offset goes into the instruction's scalar offset, with no
+  // per-lane arithmetic (the row, and with it the range check against the
+  // tile's rows, stays in the vector offset); otherwise the out-of-range
+  // offset is selected per lane for chunks past K.
+  auto issue_rows = [&](__amdgpu_buffer_rsrc_t r, int n, int8_t* buf, int kt, auto interior) {
     const int kb = kt * T::BK;
-    const bool in_k = kb + col < K;
+    if constexpr (decltype(interior)::value) {
 #pragma unroll
-    for (int i = 0; i < T::DX; ++i)
-      dma16(a.rx, buf + (wave + i * T::kWaves) * kDmaBytes,
-            in_k ? off0 + (uint32_t)(i * blk_stride + kb) : kOOB);
+      for (int i = 0; i < n; ++i)
+        dma16(r, buf + (wave + i * T::kWaves) * kDmaBytes, off0 + (uint32_t)(i * blk_stride), kb);
+    } else {
+      const bool in_k = kb + col < K;
+#pragma unroll
+      for (int i = 0; i < n; ++i)
+        dma16(r, buf + (wave + i * T::kWaves) * kDmaBytes,
+              in_k ? off0 + (uint32_t)(i * blk_stride + kb) : kOOB);
+    }
   };
-  auto issue_w = [&](const TileAddr& a, int8_t* buf, int kt) {
-    const int kb = kt * T::BK;
-    const bool in_k = kb + col < K;
-#pragma unroll
-    for (int i = 0; i < T::DW; ++i)
-      dma16(a.rw, buf + (wave + i * T::kWaves) * kDmaBytes,
-            in_k ? off0 + (uint32_t)(i * blk_stride + kb) : kOOB);
+  auto issue_x = [&](const TileAddr& a, int8_t* buf, int kt, auto interior) {
+    issue_rows(a.rx, T::DX, buf, kt, interior);
+  };
+  auto issue_w = [&](const TileAddr& a, int8_t* buf, int kt, auto interior) {
+    issue_rows(a.rw, T::DW, buf, kt, interior);
   };
   // Whole stage kt into ring slot `buf` (X rows first, then W rows).
-  auto issue = [&](const TileAddr& a, int8_t* buf, int kt) {
-    issue_x(a, buf, kt);
-    issue_w(a, buf + T::BM * T::BK, kt);
+  auto issue = [&](const TileAddr& a, int8_t* buf, int kt, auto interior) {
+    issue_x(a, buf, kt, interior);
+    issue_w(a, buf + T::BM * T::BK, kt, interior);
   };
+  // The 256x256 tile keeps one (checked) loop: it has no registers to spare
+  // for a second copy of the DMA offsets.
+  constexpr bool kSplitK = T::BM * T::BN < 256 * 256;
+  const std::false_type kChecked;
+  const std::true_type kInterior;
 
   constexpr int KSUB = T::BK / Op::kStepK;   // MFMA K steps per stage
   constexpr int CPS = Op::kStepK / 32;        // 16-byte chunks per lane and K step
@@ -361,7 +377,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
   // stage k+1 has landed (one barrier), request stage k+S into `cur` and
   // start reading stage k+1's first fragments under the MFMAs of the last K
   // step.  A stage is thus requested a full S-1 steps before it is needed.
-  auto step = [&](const TileAddr& a, int8_t* cur, int8_t* nxt, int k) {
+  auto step = [&](const TileAddr& a, int8_t* cur, int8_t* nxt, int k, auto interior) {
     if constexpr (NB == 1) {
 #pragma unroll
       for (int s = 0; s + 1 < KSUB; ++s) {
@@ -373,7 +389,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
       wait_lgkmcnt0();
       wait_vmcnt<(T::S - 2) * T::D>();
       barrier();
-      issue(a, cur, k + T::S);
+      issue(a, cur, k + T::S, interior);
       mfmas(0);
       frag(nxt, 0, 0);
       interleave1();
@@ -390,7 +406,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     wait_vmcnt<(T::S - 2) * T::D>();  // its DMAs of stage k+1 have landed
     barrier();                       // ... and everyone's
     frag(nxt, 0, KSUB & 1);
-    issue(a, cur, k + T::S);
+    issue(a, cur, k + T::S, interior);
     mfmas((KSUB - 1) & 1);
     interleave();
   };
@@ -401,7 +417,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
   // (half a stage, requested one step earlier) is on the critical path, while
   // X has two steps to land.
   auto step_split = [&](const TileAddr& a, int8_t* xc, int8_t* wc, int8_t* xn, int8_t* wn1,
-                        int k) {
+                        int k, auto interior) {
     if constexpr (NB == 1) {
 #pragma unroll
       for (int s = 0; s + 1 < KSUB; ++s) {
@@ -413,8 +429,8 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
       wait_lgkmcnt0();
       wait_vmcnt<T::DX>();
       barrier();
-      issue_w(a, wc, k + 2);
-      issue_x(a, xc, k + 3);
+      issue_w(a, wc, k + 2, interior);
+      issue_x(a, xc, k + 3, interior);
       mfmas(0);
       frag2(xn, wn1, 0, 0);
       interleave1();
@@ -431,8 +447,8 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     wait_vmcnt<T::DX>();   // everything but X_{k+2} (the last request) has landed
     barrier();
     frag2(xn, wn1, 0, KSUB & 1);
-    issue_w(a, wc, k + 2);
-    issue_x(a, xc, k + 3);
+    issue_w(a, wc, k + 2, interior);
+    issue_x(a, xc, k + 3, interior);
     mfmas((KSUB - 1) & 1);
     interleave();
   };
@@ -473,11 +489,11 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
   if constexpr (T::kSplit) {
     // X slots lds0..lds2 (X_k in slot k%3), W slots lds3, lds4 (W_k in k%2);
     // the slot pattern repeats every 6 stages.
-    issue_x(cur, lds0, 0);
-    issue_w(cur, lds3, 0);
-    issue_x(cur, lds1, 1);
-    issue_w(cur, lds4, 1);
-    issue_x(cur, lds2, 2);
+    issue_x(cur, lds0, 0, kChecked);
+    issue_w(cur, lds3, 0, kChecked);
+    issue_x(cur, lds1, 1, kChecked);
+    issue_w(cur, lds4, 1, kChecked);
+    issue_x(cur, lds2, 2, kChecked);
     wait_vmcnt<2 * T::DX + T::DW>();
     barrier();
     frag2(lds0, lds3, 0, 0);
@@ -492,36 +508,46 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     // ---- K loop ----
     if constexpr (T::kSplit) {
       const int KT6 = (KT + 5) / 6 * 6;   // padding stages read as zeros
-      for (int kt = 0; kt < KT6; kt += 6) {
-        step_split(cur, lds0, lds3, lds1, lds4, kt);
-        step_split(cur, lds1, lds4, lds2, lds3, kt + 1);
-        step_split(cur, lds2, lds3, lds0, lds4, kt + 2);
-        step_split(cur, lds0, lds4, lds1, lds3, kt + 3);
-        step_split(cur, lds1, lds3, lds2, lds4, kt + 4);
-        step_split(cur, lds2, lds4, lds0, lds3, kt + 5);
-      }
+      // six steps of the ring; the requests they make reach stage kt + 8
+      auto six = [&](int kt, auto interior) {
+        step_split(cur, lds0, lds3, lds1, lds4, kt, interior);
+        step_split(cur, lds1, lds4, lds2, lds3, kt + 1, interior);
+        step_split(cur, lds2, lds3, lds0, lds4, kt + 2, interior);
+        step_split(cur, lds0, lds4, lds1, lds3, kt + 3, interior);
+        step_split(cur, lds1, lds3, lds2, lds4, kt + 4, interior);
+        step_split(cur, lds2, lds4, lds0, lds3, kt + 5, interior);
+      };
+      int kt = 0;
+      if constexpr (kSplitK)
+        for (; kt < KT6 && (kt + 9) * T::BK <= K; kt += 6) six(kt, kInterior);
+      for (; kt < KT6; kt += 6) six(kt, kChecked);
     } else {
 #pragma unroll
-      for (int s = 0; s < T::S; ++s) issue(cur, ring[s], s);
+      for (int s = 0; s < T::S; ++s) issue(cur, ring[s], s, kChecked);
       wait_vmcnt<(T::S - 1) * T::D>();
       barrier();
       frag(ring[0], 0, 0);
       const int KTr = (KT + T::S - 1) / T::S * T::S;   // padding stages read as zeros
-      for (int kt = 0; kt < KTr; kt += T::S) {
+      // S steps of the ring; the requests they make reach stage kt + 2S - 1
+      auto round = [&](int kt, auto interior) {
         if constexpr (T::S == 2) {
-          step(cur, lds0, lds1, kt);
-          step(cur, lds1, lds0, kt + 1);
+          step(cur, lds0, lds1, kt, interior);
+          step(cur, lds1, lds0, kt + 1, interior);
         } else if constexpr (T::S == 3) {
-          step(cur, lds0, lds1, kt);
-          step(cur, lds1, lds2, kt + 1);
-          step(cur, lds2, lds0, kt + 2);
+          step(cur, lds0, lds1, kt, interior);
+          step(cur, lds1, lds2, kt + 1, interior);
+          step(cur, lds2, lds0, kt + 2, interior);
         } else {
-          step(cur, lds0, lds1, kt);
-          step(cur, lds1, lds2, kt + 1);
-          step(cur, lds2, lds3, kt + 2);
-          step(cur, lds3, lds0, kt + 3);
+          step(cur, lds0, lds1, kt, interior);
+          step(cur, lds1, lds2, kt + 1, interior);
+          step(cur, lds2, lds3, kt + 2, interior);
+          step(cur, lds3, lds0, kt + 3, interior);
         }
-      }
+      };
+      int kt = 0;
+      if constexpr (kSplitK)
+        for (; kt < KTr && (kt + 2 * T::S) * T::BK <= K; kt += T::S) round(kt, kInterior);
+      for (; kt < KTr; kt += T::S) round(kt, kChecked);
     }
     wait_vmcnt<0>();
     wait_lgkmcnt0();
@@ -552,8 +578,8 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
       }
       if constexpr (T::kSplit) {
         if (has_next) {
-          issue_x(nxt, lds0, 0);
-          issue_w(nxt, lds3, 0);
+          issue_x(nxt, lds0, 0, kChecked);
+          issue_w(nxt, lds3, 0, kChecked);
         }
       }
       // The block's channel scales and bias (as fp32) go to LDS once, so each
@@ -653,8 +679,8 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
       if (has_next) setup(t_next, nxt);
       if constexpr (T::kSplit) {
         if (has_next) {
-          issue_x(nxt, lds0, 0);
-          issue_w(nxt, lds3, 0);
+          issue_x(nxt, lds0, 0, kChecked);
+          issue_w(nxt, lds3, 0, kChecked);
         }
       }
 #pragma unroll
@@ -692,9 +718,9 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
       wait_lgkmcnt0();
       barrier();   // the epilogue's LDS regions and scales are free again
       if constexpr (T::kSplit) {
-        issue_x(cur, lds1, 1);
-        issue_w(cur, lds4, 1);
-        issue_x(cur, lds2, 2);
+        issue_x(cur, lds1, 1, kChecked);
+        issue_w(cur, lds4, 1, kChecked);
+        issue_x(cur, lds2, 2, kChecked);
         // everything older than these three requests -- the epilogue's
         // stores and X_0, W_0 of the new tile -- has completed
         wait_vmcnt<2 * T::DX + T::DW>();
