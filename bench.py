@@ -96,6 +96,54 @@ def copy_calibration(dev):
     del src, dst
 
 
+# A spin of about 1 ms queued ahead of each timed launch keeps the host's
+# launch latency out of the events: the launch is in the queue before the GPU
+# reaches the first event, as it is inside a stream of work.
+SPIN_CYCLES = 2_000_000
+
+
+def gpu_ms(fn, stream, n):
+    """Median over n runs of the GPU time of fn()'s launches (HIP events on
+    `stream`, with the queue kept busy ahead of the first event)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(n):
+        torch.cuda._sleep(SPIN_CYCLES)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return float(np.median(ts))
+
+
+def step_loop(layer_calls, stream, steps, warmup=2):
+    """Run `steps` steps of a path the way the timed step runs the fused one:
+    per linear, its launches back to back (layer_calls[i] = list of callables),
+    a HIP event before the first and after each.  Returns (wall ms per step,
+    mean ms of each linear's each launch)."""
+    nl, nph = len(layer_calls), len(layer_calls[0])
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(nph + 1)] for _ in range(nl)]
+          for _ in range(steps)]
+    for _ in range(warmup):
+        for calls in layer_calls:
+            for c in calls:
+                c()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        for i, calls in enumerate(layer_calls):
+            ev[k][i][0].record(stream)
+            for j, c in enumerate(calls):
+                c()
+                ev[k][i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) / steps * 1e3
+    ms = np.array([[[ev[k][i][j].elapsed_time(ev[k][i][j + 1]) for j in range(nph)] for i in range(nl)]
+                   for k in range(steps)]).mean(axis=0)
+    return wall_ms, ms
+
+
 def time_cold(fn, stream, scrub, reps=5):
     """Median time of fn() with the caches flushed before each run (a 512 MB
     write between runs evicts L2 and the 256 MB Infinity Cache)."""
@@ -139,19 +187,10 @@ def time_other_workloads(w8, dev, stream, iters: int = 10) -> dict:
     """Warm GEMM and quantize times of the other workloads' linears (the
     768px attention projection and MLP pair, the 1024px QKV with outliers):
     median of `iters` launches each, HIP events on the launch stream."""
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-
     def med(fn):
         fn()
         torch.cuda.synchronize()
-        ts = []
-        for _ in range(iters):
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            e1.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        return float(np.median(ts))
+        return gpu_ms(fn, stream, iters)
 
     out = {}
     for wl in datagen.WORKLOADS[1:4]:
@@ -190,68 +229,44 @@ def time_other_workloads(w8, dev, stream, iters: int = 10) -> dict:
     return out
 
 
-def time_fp8_variant(w8, layers, stream, iters: int = 10) -> dict:
+def time_fp8_variant(w8, layers, stream, steps: int) -> dict:
     """The same step with e4m3 codes (the fp8 variant): per linear, the fp8
-    activation quantizer and the fp8 GEMM with the same epilogue; weights
-    quantized to e4m3 once, before timing.  Median of `iters` launches."""
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-
-    def med(fn):
-        fn()
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(iters):
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            e1.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        return float(np.median(ts))
-
-    per, g_tot, q_tot, ops_tot = [], 0.0, 0.0, 0
+    activation quantizer and the fp8 GEMM with the same epilogue, timed like
+    the int8 step; weights quantized to e4m3 once, before timing."""
+    fp = []
     for L in layers:
-        s = L["shape"]
         cw, sw = w8.quantize_weight_fp8(L["wbf"])
         cx, sx = w8.quantize_act_fp8(L["x"])
-        g = med(lambda: w8.linear_fp8(cx, sx, cw, sw, L["b"], y=L["y"]))
-        q = med(lambda: w8.quantize_act_fp8(L["x"], cx, sx))
+        fp.append((cw, sw, cx, sx))
+    calls = [[lambda L=L, f=f: w8.quantize_act_fp8(L["x"], f[2], f[3]),
+              lambda L=L, f=f: w8.linear_fp8(f[2], f[3], f[0], f[1], L["b"], y=L["y"])]
+             for L, f in zip(layers, fp)]
+    wall_ms, ms = step_loop(calls, stream, steps)
+    per, ops_tot = [], 0
+    for L, (q, g) in zip(layers, ms):
+        s = L["shape"]
         ops = 2 * s.M * s.N * s.K
         per.append({"linear": s.name, "gemm_us": round(g * 1e3, 2), "gemm_tops": round(ops / g / 1e9, 1),
                     "quant_us": round(q * 1e3, 2)})
-        g_tot += g
-        q_tot += q
         ops_tot += ops
-        del cw, cx
-    return {"gemm_tops": round(ops_tot / g_tot / 1e9, 1),
+    g_tot, q_tot = float(ms[:, 1].sum()), float(ms[:, 0].sum())
+    del fp
+    return {"value": round(ops_tot / wall_ms / 1e9, 1), "ms_per_step": round(wall_ms, 4),
+            "gemm_tops": round(ops_tot / g_tot / 1e9, 1),
             "frac_of_fp8_peak": round(ops_tot / g_tot / 1e9 / MFMA_INT8_PEAK_TOPS, 4),
             "linear_tops": round(ops_tot / (g_tot + q_tot) / 1e9, 1), "per_linear": per,
             "note": "e4m3 codes, v_mfma_f32_32x32x64_f8f6f4, same tiles and epilogue; "
                     "MI355X dense fp8 peak = int8 peak = 5.0 P"}
 
 
-def median_ms(fn, stream, n):
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ts = []
-    for _ in range(n):
-        e0.record(stream)
-        fn()
-        e1.record(stream)
-        e1.synchronize()
-        ts.append(e0.elapsed_time(e1))
-    return float(np.median(ts))
-
-
-def bf16_comparator(layers, per, stream, steps) -> float:
-    """torch F.linear (hipBLASLt bf16) on the same shapes: median per linear."""
-    for L in layers:
-        torch.nn.functional.linear(L["x"], L["wbf"], L["b"])
-    torch.cuda.synchronize()
-    total = 0.0
-    for p, L in zip(per, layers):
-        t = median_ms(lambda: torch.nn.functional.linear(L["x"], L["wbf"], L["b"]), stream, max(3, steps // 2))
-        p["bf16_us"] = round(t * 1e3, 2)
-        total += t
-    return total
+def bf16_comparator(layers, per, stream, steps) -> tuple:
+    """torch F.linear (hipBLASLt bf16) on the same shapes, run as a step like
+    the fused one.  Returns (sum of per-linear mean ms, wall ms per step)."""
+    calls = [[lambda L=L: torch.nn.functional.linear(L["x"], L["wbf"], L["b"])] for L in layers]
+    wall_ms, ms = step_loop(calls, stream, steps)
+    for p, t in zip(per, ms[:, 0]):
+        p["bf16_us"] = round(float(t) * 1e3, 2)
+    return float(ms[:, 0].sum()), wall_ms
 
 
 def cold_timings(w8, layers, per, stream, dev, step_ops, q_bytes) -> dict:
@@ -274,19 +289,17 @@ def cold_timings(w8, layers, per, stream, dev, step_ops, q_bytes) -> dict:
             "note": "median of 5 runs per launch, 512 MB cache scrub before each"}
 
 
-def slow_path(w8, layers, per, stream, steps) -> float:
-    """The same linears through quantize -> dequantize to bf16 -> bf16 GEMM."""
-    total = 0.0
-    for p, L in zip(per, layers):
-        scratch = {}
-        fn = lambda: w8.dequant_bf16_linear(L["x"], L["wq"], L["ws"], L["b"], scratch)
-        fn()
-        torch.cuda.synchronize()
-        t = median_ms(fn, stream, max(3, steps // 2))
-        p["dequant_bf16_us"] = round(t * 1e3, 2)
-        total += t
-        del scratch
-    return total
+def slow_path(w8, layers, per, stream, steps) -> tuple:
+    """The same linears through quantize -> dequantize to bf16 -> bf16 GEMM,
+    run as a step.  Returns (sum of per-linear mean ms, wall ms per step)."""
+    scratch = [{} for _ in layers]
+    calls = [[lambda L=L, sc=sc: w8.dequant_bf16_linear(L["x"], L["wq"], L["ws"], L["b"], sc)]
+             for L, sc in zip(layers, scratch)]
+    wall_ms, ms = step_loop(calls, stream, steps)
+    for p, t in zip(per, ms[:, 0]):
+        p["dequant_bf16_us"] = round(float(t) * 1e3, 2)
+    del scratch
+    return float(ms[:, 0].sum()), wall_ms
 
 
 def main():
@@ -375,7 +388,7 @@ def main():
     bf_total = None
     if extras:
         log("bf16 comparator")
-        bf_total = bf16_comparator(layers, per, stream, args.steps)
+        bf_total, bf_wall = bf16_comparator(layers, per, stream, args.steps)
 
     # ---- cold caches: GEMM and quantize with L2 and Infinity Cache flushed ----
     cold = None
@@ -386,12 +399,12 @@ def main():
     slow_total = None
     if extras:
         log("dequantize-to-bf16 comparator")
-        slow_total = slow_path(w8, layers, per, stream, args.steps)
+        slow_total, slow_wall = slow_path(w8, layers, per, stream, args.steps)
 
     fp8 = None
     if extras:
         log("fp8 variant")
-        fp8 = time_fp8_variant(w8, layers, stream)
+        fp8 = time_fp8_variant(w8, layers, stream, args.steps)
 
     other = None
     if extras and not args.no_other:
@@ -437,9 +450,11 @@ def main():
         "vs_dequant_bf16_path": None if slow_total is None else {
             "tops": round(step_ops / slow_total / 1e9, 1),
             "speedup_full_linear": round(slow_total / (gemm_total_ms + q_total_ms), 3),
+            "step_ms": round(slow_wall, 4), "speedup_step": round(slow_wall / ms_per_step, 3),
             "path": "quantize_act + dequantize X and W to bf16 + torch F.linear"},
         "vs_bf16": None if bf_total is None else {
             "bf16_torch_linear_tops": round(step_ops / bf_total / 1e9, 1),
+            "step_ms": round(bf_wall, 4), "speedup_step": round(bf_wall / ms_per_step, 3),
             "speedup_full_linear": round(bf_total / (gemm_total_ms + q_total_ms), 3),
             "speedup_gemm_only": round(bf_total / gemm_total_ms, 3)},
         "per_linear": per,
