@@ -56,6 +56,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kWave = 64;
 constexpr int kNumXcd = 8;
 constexpr int kGroupM = 4;
+constexpr int kCUs = 256;               // compute units of an MI355X (one workgroup each)
 constexpr int kDmaBytes = kWave * 16;    // one wavefront DMA: 64 lanes x 16 B
 constexpr uint32_t kOOB = 0x80000000u;    // buffer offset beyond any tile: reads as zero
 constexpr int kRsrcWord3 = 0x00020000;    // raw buffer, 32-bit data format (gfx9 family)
@@ -196,17 +197,34 @@ struct OpF8 {
 // groups of kGroupM tile rows (tiles resident on one XCD share X and W panels
 // in its L2).  A workgroup on XCD x only ever gets tiles of XCD x's range:
 // grid sizes are multiples of 8 whenever tile counts are.
+#ifndef ROTATE_COLS
+#define ROTATE_COLS 1
+#endif
 __device__ __forceinline__ void tile_origin(int t, int tiles_m, int tiles_n, int bm, int bn,
                                             int& m0, int& n0) {
   const int ntiles = tiles_m * tiles_n;
-  if (ntiles % kNumXcd == 0) t = (t % kNumXcd) * (ntiles / kNumXcd) + t / kNumXcd;
+  int rot = 0;
+  if (ntiles % kNumXcd == 0) {
+    const int x = t % kNumXcd;
+    t = x * (ntiles / kNumXcd) + t / kNumXcd;
+#if ROTATE_COLS
+    // XCD x starts its column walk x rounds later (a round = the 32
+    // workgroups of an XCD = 32 / kGroupM columns): the weight columns an XCD
+    // reaches in a round were first read by its neighbour a round earlier
+    // and come from the Infinity Cache, where without the rotation every XCD
+    // would wait on HBM for the same new columns in every round.  Only when
+    // every XCD owns whole row groups, so that a group's tiles all rotate
+    // alike and the mapping stays one to one.
+    if ((ntiles / kNumXcd) % (kGroupM * tiles_n) == 0) rot = x * (kCUs / kNumXcd / kGroupM);
+#endif
+  }
   const int per_group = kGroupM * tiles_n;
   const int group = t / per_group;
   const int first_m = group * kGroupM;
   const int gsize = min(tiles_m - first_m, kGroupM);
   const int in_group = t - group * per_group;
   m0 = (first_m + in_group % gsize) * bm;
-  n0 = (in_group / gsize) * bn;
+  n0 = ((in_group / gsize + rot) % tiles_n) * bn;
 }
 
 // Persistent kernel: gridDim.x workgroups (at most one per CU) walk the
@@ -895,7 +913,6 @@ constexpr Plan kPlans[] = {
     {kSplit256, kTail128x256}, {kSplit256, -1}, {kWhole256, kTail128x256}, {kWhole256, -1},
     {k192, -1}, {kTail128x256, -1}, {k256x128, -1}, {k128, -1}, {k64, -1}};
 constexpr int kNumPlans = sizeof(kPlans) / sizeof(kPlans[0]);
-constexpr int kCUs = 256;
 
 // Leading columns of main tiles that form whole waves (0: no useful split).
 int64_t main_columns(const TileDesc& d, int64_t M, int64_t N) {
