@@ -171,6 +171,20 @@ def test_main_plus_tail_split(w, M, N, K):
         run_linear_check(w, x, W, b, rows, tile=tile, label=f"split tile{tile}")
 
 
+@pytest.mark.parametrize("M,N,K", [(16384, 576, 256), (8192, 2304, 320), (8192, 768, 272)])
+def test_rotated_column_walk(w, M, N, K):
+    """Grids in which every XCD owns whole groups of tile rows, so the
+    per-XCD rotation of the column walk applies (with 1 and 2 groups per XCD
+    and column counts that the rotation wraps around): every output tile must
+    still be computed exactly once."""
+    x = datagen.random_bf16((M, K), seed=M + N)
+    W = datagen.random_bf16((N, K), seed=N + 3, std=0.02)
+    b = datagen.random_bf16((N,), seed=K + 5, std=0.01)
+    rows = sample_rows(M, 40, 11)
+    for tile in range(w.num_tiles()):
+        run_linear_check(w, x, W, b, rows, tile=tile, label=f"rotated walk tile{tile}")
+
+
 def test_special_rows(w):
     """Zero rows give exactly the bias; huge, tiny (subnormal-scale) and
     single-spike rows quantize bit-exactly."""
