@@ -933,14 +933,18 @@ int64_t main_columns(const TileDesc& d, int64_t M, int64_t N) {
 
 // Relative throughput of one CU running a configuration's tiles, against
 // the 256x256 split-ring tile (measured on MI355X at K = 3072 and 12288 on
-// the DiT shapes; the persistent grid runs one tile per CU at a time).
+// the DiT shapes, with the weights cold as they are at every use inside a
+// model; the persistent grid runs one tile per CU at a time).  With cold
+// weights 256x128 tiles beat 128x256 ones on the 768px projection and
+// MLP-down (they read half the weight rows per tile), with warm ones the
+// order is the other way round.
 double cfg_efficiency(int cfg) {
   switch (cfg) {
     case kSplit256: return 1.0;
     case kWhole256: return 0.97;
     case k192: return 1.0;
     case kTail128x256: return 0.70;
-    case k256x128: return 0.63;
+    case k256x128: return 0.73;
     case k128: return 0.54;
     default: return 0.27;
   }
