@@ -27,6 +27,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -142,6 +143,36 @@ def step_loop(layer_calls, stream, steps, warmup=2):
     ms = np.array([[[ev[k][i][j].elapsed_time(ev[k][i][j + 1]) for j in range(nph)] for i in range(nl)]
                    for k in range(steps)]).mean(axis=0)
     return wall_ms, ms
+
+
+def sample_sclk(step, n_steps: int = 600, samples: int = 4) -> dict | None:
+    """Shader clock while the step loop runs: `n_steps` steps are queued
+    (about half a second of GPU work), then `amd-smi metric --clock` is read
+    `samples` times from a child process; the mean over the XCDs' gfx clocks
+    of each sample is kept.  None if the tool is missing or fails."""
+    for _ in range(n_steps):
+        step()
+    vals = []
+    try:
+        for _ in range(samples):
+            r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True,
+                               text=True, timeout=20)
+            if r.returncode != 0:
+                break
+            data = json.loads(r.stdout)
+            gpus = data["gpu_data"] if isinstance(data, dict) else data
+            clk = gpus[0]["clock"]
+            xcd = [v["clk"]["value"] for k, v in clk.items() if k.startswith("gfx_")]
+            if xcd:
+                vals.append(sum(xcd) / len(xcd))
+    except (OSError, ValueError, KeyError, IndexError, TypeError, subprocess.SubprocessError):
+        pass
+    torch.cuda.synchronize()
+    if not vals:
+        return None
+    return {"mhz": [round(v) for v in vals], "median_mhz": round(float(np.median(vals))),
+            "source": "amd-smi metric --clock, mean over the XCDs' gfx clocks, read while "
+                      f"{n_steps} steps run"}
 
 
 def time_cold(fn, stream, scrub, reps=5):
@@ -400,6 +431,7 @@ def main():
     q_total_ms = float(q_ms.mean(axis=0).sum())
 
     extras = not args.only_step
+    sclk = sample_sclk(step) if extras else None
     # ---- bf16 comparator: torch F.linear, same shapes, same GPU ----
     bf_total = None
     if extras:
@@ -461,6 +493,9 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(q_bytes / q_total_ms / 1e6 / HBM_PEAK_GBS, 4)},
         "cold": cold,
+        "sclk": sclk,
+        "frac_at_sclk": None if sclk is None else round(
+            gemm_tops / (MFMA_INT8_PEAK_TOPS * sclk["median_mhz"] / 2400.0), 4),
         "other_workloads": other,
         "fp8_variant": fp8,
         "vs_dequant_bf16_path": None if slow_total is None else {
