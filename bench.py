@@ -172,7 +172,7 @@ def sample_sclk(step, n_steps: int = 600, samples: int = 4) -> dict | None:
         return None
     return {"mhz": [round(v) for v in vals], "median_mhz": round(float(np.median(vals))),
             "source": "amd-smi metric --clock, mean over the XCDs' gfx clocks, read while "
-                      f"{n_steps} steps run"}
+                      f"{n_steps} steps run (the tool's instantaneous reading, not an average)"}
 
 
 def time_cold(fn, stream, scrub, reps=5):
@@ -494,8 +494,6 @@ def main():
                      "frac": round(q_bytes / q_total_ms / 1e6 / HBM_PEAK_GBS, 4)},
         "cold": cold,
         "sclk": sclk,
-        "frac_at_sclk": None if sclk is None else round(
-            gemm_tops / (MFMA_INT8_PEAK_TOPS * sclk["median_mhz"] / 2400.0), 4),
         "other_workloads": other,
         "fp8_variant": fp8,
         "vs_dequant_bf16_path": None if slow_total is None else {
