@@ -197,26 +197,22 @@ struct OpF8 {
 // groups of kGroupM tile rows (tiles resident on one XCD share X and W panels
 // in its L2).  A workgroup on XCD x only ever gets tiles of XCD x's range:
 // grid sizes are multiples of 8 whenever tile counts are.
-#ifndef ROTATE_COLS
-#define ROTATE_COLS 1
-#endif
 __device__ __forceinline__ void tile_origin(int t, int tiles_m, int tiles_n, int bm, int bn,
                                             int& m0, int& n0) {
   const int ntiles = tiles_m * tiles_n;
-  int rot = 0;
   if (ntiles % kNumXcd == 0) {
-    const int x = t % kNumXcd;
-    t = x * (ntiles / kNumXcd) + t / kNumXcd;
-#if ROTATE_COLS
-    // XCD x starts its column walk x rounds later (a round = the 32
-    // workgroups of an XCD = 32 / kGroupM columns): the weight columns an XCD
-    // reaches in a round were first read by its neighbour a round earlier
-    // and come from the Infinity Cache, where without the rotation every XCD
-    // would wait on HBM for the same new columns in every round.  Only when
-    // every XCD owns whole row groups, so that a group's tiles all rotate
-    // alike and the mapping stays one to one.
-    if ((ntiles / kNumXcd) % (kGroupM * tiles_n) == 0) rot = x * (kCUs / kNumXcd / kGroupM);
-#endif
+    // XCD x walks its own range of tiles starting x rounds in (a round = the
+    // 32 tiles its workgroups take at once), wrapping around: otherwise all
+    // XCDs reach the same new weight columns in the same round and all wait
+    // on HBM for them (the weights are cold at every use inside a model);
+    // rotated, the columns an XCD reaches were read by another XCD a round
+    // earlier and come from the Infinity Cache.  A cyclic shift within each
+    // XCD's range keeps the mapping one to one; it is applied when the range
+    // is whole rounds, so that every round stays one compact block of tiles.
+    constexpr int kRound = kCUs / kNumXcd;
+    const int x = t % kNumXcd, per_xcd = ntiles / kNumXcd;
+    const int shift = per_xcd % kRound == 0 ? x * kRound : 0;
+    t = x * per_xcd + (t / kNumXcd + shift) % per_xcd;
   }
   const int per_group = kGroupM * tiles_n;
   const int group = t / per_group;
@@ -224,7 +220,7 @@ __device__ __forceinline__ void tile_origin(int t, int tiles_m, int tiles_n, int
   const int gsize = min(tiles_m - first_m, kGroupM);
   const int in_group = t - group * per_group;
   m0 = (first_m + in_group % gsize) * bm;
-  n0 = ((in_group / gsize + rot) % tiles_n) * bn;
+  n0 = (in_group / gsize) * bn;
 }
 
 // Persistent kernel: gridDim.x workgroups (at most one per CU) walk the
