@@ -246,6 +246,13 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
   __shared__ __attribute__((aligned(16))) int8_t lds2[T::kSlots > 2 ? kArr012 : 16];
   __shared__ __attribute__((aligned(16))) int8_t lds3[T::kSlots > 3 ? kArr34 : 16];
   __shared__ __attribute__((aligned(16))) int8_t lds4[T::kSlots > 4 ? kArr34 : 16];
+  // Epilogue transpose regions and channel scales in an array of their own
+  // where the split ring leaves room (256x192 int8): LDS writes to the ring's
+  // slots would have to wait for the next tile's first requests in flight,
+  // which the compiler cannot tell apart from them.
+  constexpr int kEpiBytes = 8 * 32 * 64 + 2 * T::BN * 4;
+  constexpr bool kEpiOwn = T::kSplit && 3 * kArr012 + 2 * kArr34 + kEpiBytes <= 160 * 1024;
+  __shared__ __attribute__((aligned(16))) int8_t lds_epi[kEpiOwn ? kEpiBytes : 16];
   int8_t* const ring[4] = {lds0, lds1, lds2, lds3};
 
   const int ntiles = tiles_m * tiles_n;
@@ -281,6 +288,16 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
   static_assert(2 * DXk + DWk <= 63 && 2 * DWk + DXk <= 63, "vmcnt range");
   static_assert((kDmaWaves * T::kDmaRows) % 16 == 0, "one swizzle phase per DMA block set");
   const bool dma_wave = !kHalfDma || wave < kDmaWaves;
+  // Split ring with the bf16 epilogue: the epilogue's stores are buffer
+  // stores, exactly two per 32x32 tile and wavefront, so the hand-over can
+  // wait for the new tile's first requests without waiting for the stores
+  // (the counter completes in order).  Offsets are 32-bit: the host sends
+  // the plain path (vec_store = 0) when BM * ldy * 2 >= 2^31.
+#ifndef COUNTED_STORES
+#define COUNTED_STORES 1
+#endif
+  constexpr bool kCountedStores = COUNTED_STORES && T::kSplit && EPI != Epilogue::kRawI32;
+  constexpr int kStores = 2 * T::FM * T::FN;   // store instructions per wavefront and tile
   const int dma_r = (wave % kDmaWaves) * T::kDmaRows + lane / T::CPR;
   const int col = swz<T::CPR>(dma_r, lane % T::CPR) * 16;   // K byte offset within a stage
   const uint32_t off0 = (uint32_t)(dma_r * K + col);
@@ -343,6 +360,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
   };
   constexpr int DA = kWAhead ? DWk : DXk;   // requests per stage of A, B
   constexpr int DB = kWAhead ? DXk : DWk;
+  static_assert(2 * DA + DB + kStores <= 63, "vmcnt range");
   // Whole stage kt into ring slot `buf` (X rows first, then W rows).
   auto issue = [&](const TileAddr& a, int8_t* buf, int kt, auto interior) {
     issue_x(a, buf, kt, interior);
@@ -539,24 +557,28 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
   constexpr bool kSbAfter = T::kWaves * kRegion + 2 * T::BN * 4 <= kArr012;
   static_assert(T::kWaves * kRegion <= kArr012, "regions fit in one array");
   static_assert(kSbAfter || (!T::kSplit && 2 * T::BN * 4 <= kArr012), "scales and bias fit");
-  int8_t* const reg_a = T::kSplit ? lds1 : lds0;
+  static_assert(!kEpiOwn || T::kWaves == 8, "regions of eight wavefronts");
+  int8_t* const reg_a = kEpiOwn ? lds_epi : T::kSplit ? lds1 : lds0;
   // channel scales and biases (fp32) follow the regions, else take the next array
-  int8_t* const sb_arr = kSbAfter ? reg_a + T::kWaves * kRegion : lds1;
+  int8_t* const sb_arr = kEpiOwn || kSbAfter ? reg_a + T::kWaves * kRegion : lds1;
 
   // Dequant scalars of a tile, requested one tile ahead so that their
   // latency hides under a K loop: per-token scales of the rows this lane
-  // holds, and (threads below BN) one channel's scale and bias.
-  float sa_n[T::FM], sw_n = 0.0f, b_n = 0.0f;
+  // holds, and (threads below BN) one channel's scale and bias.  Nothing
+  // is done with them until that tile's epilogue (the bias stays in bf16
+  // bits), so no wait for them falls inside this epilogue.
+  float sa_n[T::FM], sw_n = 0.0f;
+  uint32_t b_n = 0;
   auto load_scalars = [&](const TileAddr& a) {
     if constexpr (EPI != Epilogue::kRawI32) {
 #pragma unroll
       for (int i = 0; i < T::FM; ++i) sa_n[i] = sx[min(a.m0 + wm * T::TM + i * 32 + row_in, M - 1)];
       static_assert(T::BN <= T::kThreads, "one thread per channel of the block");
       sw_n = 0.0f;
-      b_n = 0.0f;
+      b_n = 0;
       if (tid < T::BN && a.n0 + tid < N) {
         sw_n = sw[a.n0 + tid];
-        if (bias != nullptr) b_n = bf16_to_float(bias[a.n0 + tid]);
+        if (bias != nullptr) b_n = bias[a.n0 + tid];
       }
     }
   };
@@ -642,6 +664,12 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     barrier();   // every DMA and fragment read of this tile is done
 
     const int m0 = cur.m0, n0 = cur.n0;
+    // output rows of this tile as a buffer range (bf16, ldy apart)
+    __amdgpu_buffer_rsrc_t y_rsrc;
+    if constexpr (kCountedStores)
+      y_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<uint16_t*>(out) + (int64_t)m0 * ldy, (short)0,
+          (int)((uint32_t)min(T::BM, M - m0) * (uint32_t)ldy * 2u), kRsrcWord3);
     const int t_next = t + gridDim.x;
     const bool has_next = t_next < ntiles;
 
@@ -658,7 +686,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
       float sa[T::FM];
 #pragma unroll
       for (int i = 0; i < T::FM; ++i) sa[i] = sa_n[i];
-      const float sw_l = sw_n, b_l = b_n;
+      const float sw_l = sw_n, b_l = bf16_to_float((uint16_t)b_n);
       TileAddr nxt;
       if (has_next) {
         setup(t_next, nxt);
@@ -738,11 +766,23 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
             }
             v[1] = v4i{v[1][2], v[1][3], v[1][0], v[1][1]};   // rows 16..31: halves swapped
             const int n = n0 + nj + (e_lane % 4) * 8;   // this lane's 8 channels when storing
+            if constexpr (kCountedStores) {
+              // exactly two store instructions per 32x32 tile: rows past M
+              // fall outside the tile's buffer range, channels past N go to
+              // the out-of-range offset
 #pragma unroll
-            for (int it = 0; it < 2; ++it) {
-              const int m = mb + it * 16 + e_lane / 4;
-              if (m < M && n < N)
-                *reinterpret_cast<v4i*>(reinterpret_cast<uint16_t*>(out) + (int64_t)m * ldy + n) = v[it];
+              for (int it = 0; it < 2; ++it) {
+                const int r = mb - m0 + it * 16 + e_lane / 4;
+                const uint32_t o = n < N ? (uint32_t)(r * ldy + n) * 2u : kOOB;
+                __builtin_amdgcn_raw_buffer_store_b128(v[it], y_rsrc, o, 0, 0);
+              }
+            } else {
+#pragma unroll
+              for (int it = 0; it < 2; ++it) {
+                const int m = mb + it * 16 + e_lane / 4;
+                if (m < M && n < N)
+                  *reinterpret_cast<v4i*>(reinterpret_cast<uint16_t*>(out) + (int64_t)m * ldy + n) = v[it];
+              }
             }
           } else {
             const int m = mb + e_row;
@@ -810,9 +850,11 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
           issue_a(cur, lds1, 1, kChecked);
           issue_b(cur, lds4, 1, kChecked);
           issue_a(cur, lds2, 2, kChecked);
-          // everything older than these three requests -- the epilogue's
-          // stores and A_0, B_0 of the new tile -- has completed
-          wait_vmcnt<2 * DA + DB>();
+          // A_0, B_0 of the new tile have landed (with counted stores these
+          // drain under the new tile's first stage; otherwise they are
+          // older than A_0, B_0 for the counter and are waited for too)
+          if (kCountedStores && vec_store) wait_vmcnt<2 * DA + DB + kStores>();
+          else wait_vmcnt<2 * DA + DB>();
         }
         barrier();
         frag_ab(lds0, lds3, 0, 0);
@@ -844,12 +886,16 @@ hipError_t launch_t(Epilogue epi, const int8_t* xq, const int8_t* wq, const floa
   const dim3 block(T::kThreads);
   const uintptr_t o = reinterpret_cast<uintptr_t>(out);
   if (epi == Epilogue::kBf16ScaleBias) {
-    const int vec = (ldy % 8 == 0) && (o % 16 == 0);
+    // 16-byte stores; the split ring's buffer stores take 32-bit offsets
+    // within a tile's rows
+    const int vec = (ldy % 8 == 0) && (o % 16 == 0) && (int64_t)T::BM * ldy * 2 < (int64_t(1) << 31);
     hipLaunchKernelGGL((gemm_i8_kernel<T, Epilogue::kBf16ScaleBias, Op>), grid, block, 0, stream, xq,
                        wq, sx, sw, bias, out, (int)M, (int)N, (int)K, (int)ldy, tiles_m, tiles_n,
                        vec);
   } else if (epi == Epilogue::kBf16GeluScaleBias) {
-    const int vec = (ldy % 8 == 0) && (o % 16 == 0);
+    // 16-byte stores; the split ring's buffer stores take 32-bit offsets
+    // within a tile's rows
+    const int vec = (ldy % 8 == 0) && (o % 16 == 0) && (int64_t)T::BM * ldy * 2 < (int64_t(1) << 31);
     hipLaunchKernelGGL((gemm_i8_kernel<T, Epilogue::kBf16GeluScaleBias, Op>), grid, block, 0, stream,
                        xq, wq, sx, sw, bias, out, (int)M, (int)N, (int)K, (int)ldy, tiles_m,
                        tiles_n, vec);
