@@ -358,6 +358,21 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     if constexpr (kWAhead) issue_x(a, buf, kt, interior);
     else issue_w(a, buf, kt, interior);
   };
+  // With the epilogue in an LDS array of its own, the ring's requests for
+  // stages past the tile's last one (KT6 .. KT6 + 2) are the next tile's
+  // stages 0 .. 2, into exactly the slots its first steps read: the next
+  // tile's start is requested during this tile's last steps, and the tile
+  // boundary needs no requests, waits or barriers of its own.
+  TileAddr pre;        // the next tile (rows out of range when there is none)
+  int kt6_cur = 0;     // stages of the current tile's ring walk
+  auto issue_a_at = [&](const TileAddr& a, int8_t* buf, int s, auto interior) {
+    if (s >= kt6_cur) issue_a(pre, buf, s - kt6_cur, std::false_type{});
+    else issue_a(a, buf, s, interior);
+  };
+  auto issue_b_at = [&](const TileAddr& a, int8_t* buf, int s, auto interior) {
+    if (s >= kt6_cur) issue_b(pre, buf, s - kt6_cur, std::false_type{});
+    else issue_b(a, buf, s, interior);
+  };
   constexpr int DA = kWAhead ? DWk : DXk;   // requests per stage of A, B
   constexpr int DB = kWAhead ? DXk : DWk;
   static_assert(2 * DA + DB + kStores <= 63, "vmcnt range");
@@ -508,8 +523,9 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
   // (requested one step earlier) is on the critical path, while A has two
   // steps to land.
   auto step_split = [&](const TileAddr& a, int8_t* ac, int8_t* bc, int8_t* an, int8_t* bn1,
-                        int k, auto interior, auto role) {
+                        int k, auto interior, auto role, auto fin) __attribute__((always_inline)) {
     constexpr bool kDma = decltype(role)::value;
+    constexpr bool kFin = decltype(fin)::value;   // last six steps: requests may reach the next tile
     if constexpr (NB == 1) {
 #pragma unroll
       for (int s = 0; s + 1 < KSUB; ++s) {
@@ -521,7 +537,10 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
       wait_lgkmcnt0();
       if constexpr (kDma) wait_vmcnt<DA>();
       barrier();
-      if constexpr (kDma) {
+      if constexpr (kDma && kFin) {
+        issue_b_at(a, bc, k + 2, interior);
+        issue_a_at(a, ac, k + 3, interior);
+      } else if constexpr (kDma) {
         issue_b(a, bc, k + 2, interior);
         issue_a(a, ac, k + 3, interior);
       }
@@ -541,7 +560,10 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     if constexpr (kDma) wait_vmcnt<DA>();   // everything but A_{k+2} (the last request) has landed
     barrier();
     frag_ab(an, bn1, 0, KSUB & 1);
-    if constexpr (kDma) {
+    if constexpr (kDma && kFin) {
+      issue_b_at(a, bc, k + 2, interior);
+      issue_a_at(a, ac, k + 3, interior);
+    } else if constexpr (kDma) {
       issue_b(a, bc, k + 2, interior);
       issue_a(a, ac, k + 3, interior);
     }
@@ -611,19 +633,34 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     if constexpr (T::kSplit) {
       const int KT6 = (KT + 5) / 6 * 6;   // padding stages read as zeros
       // six steps of the ring; the requests they make reach stage kt + 8
-      auto kloop = [&](auto role) {
-        auto six = [&](int kt, auto interior) {
-          step_split(cur, lds0, lds3, lds1, lds4, kt, interior, role);
-          step_split(cur, lds1, lds4, lds2, lds3, kt + 1, interior, role);
-          step_split(cur, lds2, lds3, lds0, lds4, kt + 2, interior, role);
-          step_split(cur, lds0, lds4, lds1, lds3, kt + 3, interior, role);
-          step_split(cur, lds1, lds3, lds2, lds4, kt + 4, interior, role);
-          step_split(cur, lds2, lds4, lds0, lds3, kt + 5, interior, role);
+      auto kloop = [&](auto role) __attribute__((always_inline)) {
+        auto six = [&](int kt, auto interior, auto fin) __attribute__((always_inline)) {
+          step_split(cur, lds0, lds3, lds1, lds4, kt, interior, role, fin);
+          step_split(cur, lds1, lds4, lds2, lds3, kt + 1, interior, role, fin);
+          step_split(cur, lds2, lds3, lds0, lds4, kt + 2, interior, role, fin);
+          step_split(cur, lds0, lds4, lds1, lds3, kt + 3, interior, role, fin);
+          step_split(cur, lds1, lds3, lds2, lds4, kt + 4, interior, role, fin);
+          step_split(cur, lds2, lds4, lds0, lds3, kt + 5, interior, role, fin);
         };
         int kt = 0;
         if constexpr (kSplitK)
-          for (; kt < KT6 && (kt + 9) * T::BK <= K; kt += 6) six(kt, kInterior);
-        for (; kt < KT6; kt += 6) six(kt, kChecked);
+          for (; kt < KT6 && (kt + 9) * T::BK <= K; kt += 6) six(kt, kInterior, std::false_type{});
+        if constexpr (kEpiOwn) {
+          for (; kt < KT6 - 6; kt += 6) six(kt, kChecked, std::false_type{});
+          if constexpr (decltype(role)::value) {
+            kt6_cur = KT6;
+            if (t + (int)gridDim.x < ntiles) {
+              setup(t + (int)gridDim.x, pre);
+            } else {
+              pre.m0 = pre.n0 = 0;
+              pre.rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(X), (short)0, 0, kRsrcWord3);
+              pre.rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(W), (short)0, 0, kRsrcWord3);
+            }
+          }
+          six(kt, kChecked, std::true_type{});
+        } else {
+          for (; kt < KT6; kt += 6) six(kt, kChecked, std::false_type{});
+        }
       };
       if constexpr (kHalfDma) {
         if (dma_wave) kloop(kDmaRole);
@@ -659,9 +696,11 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
         for (; kt < KTr && (kt + 2 * T::S) * T::BK <= K; kt += T::S) round(kt, kInterior);
       for (; kt < KTr; kt += T::S) round(kt, kChecked);
     }
-    wait_vmcnt<0>();
-    wait_lgkmcnt0();
-    barrier();   // every DMA and fragment read of this tile is done
+    if constexpr (!kEpiOwn) {
+      wait_vmcnt<0>();
+      wait_lgkmcnt0();
+      barrier();   // every DMA and fragment read of this tile is done
+    }
 
     const int m0 = cur.m0, n0 = cur.n0;
     // output rows of this tile as a buffer range (bf16, ldy apart)
@@ -692,7 +731,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
         setup(t_next, nxt);
         load_scalars(nxt);
       }
-      if constexpr (T::kSplit) {
+      if constexpr (T::kSplit && !kEpiOwn) {
         if (has_next && dma_wave) {
           issue_a(nxt, lds0, 0, kChecked);
           issue_b(nxt, lds3, 0, kChecked);
@@ -805,7 +844,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     } else {
       TileAddr nxt;
       if (has_next) setup(t_next, nxt);
-      if constexpr (T::kSplit) {
+      if constexpr (T::kSplit && !kEpiOwn) {
         if (has_next && dma_wave) {
           issue_a(nxt, lds0, 0, kChecked);
           issue_b(nxt, lds3, 0, kChecked);
@@ -842,7 +881,11 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     }
 
     // ---- hand over to the next tile ----
-    if (has_next) {
+    if constexpr (kEpiOwn) {
+      // the next tile's stages 0..2 were requested during the last steps of
+      // this one, and stage 0 had landed by the last step's barrier
+      if (has_next) frag_ab(lds0, lds3, 0, 0);
+    } else if (has_next) {
       wait_lgkmcnt0();
       barrier();   // the epilogue's LDS regions and scales are free again
       if constexpr (T::kSplit) {
@@ -861,6 +904,9 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
       }
     }
   }
+  // requests of a last tile's final steps (the next tile's stages, out of
+  // range) may still be writing LDS: drain them before the workgroup ends
+  wait_vmcnt<0>();
 }
 
 // Compute units of the current device (each persistent workgroup takes one).
