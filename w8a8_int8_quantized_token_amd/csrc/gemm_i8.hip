@@ -293,10 +293,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
   // wait for the new tile's first requests without waiting for the stores
   // (the counter completes in order).  Offsets are 32-bit: the host sends
   // the plain path (vec_store = 0) when BM * ldy * 2 >= 2^31.
-#ifndef COUNTED_STORES
-#define COUNTED_STORES 1
-#endif
-  constexpr bool kCountedStores = COUNTED_STORES && T::kSplit && EPI != Epilogue::kRawI32;
+  constexpr bool kCountedStores = T::kSplit && EPI != Epilogue::kRawI32;
   constexpr int kStores = 2 * T::FM * T::FN;   // store instructions per wavefront and tile
   const int dma_r = (wave % kDmaWaves) * T::kDmaRows + lane / T::CPR;
   const int col = swz<T::CPR>(dma_r, lane % T::CPR) * 16;   // K byte offset within a stage
@@ -517,13 +514,39 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     interleave(kDmaRole);
   };
 
+  // Dequant scalars of the current tile: per-token scales of the rows this
+  // lane holds, and (threads below BN) one channel's scale and bias (kept
+  // as bf16 bits until the epilogue).  With the epilogue's own LDS they are
+  // requested at the first step of the tile's last six, after that step's
+  // wait and before its requests, so the next explicit wait covers them;
+  // otherwise at the tile's start (its K loop ends with a full wait).
+  // Requested and used within one tile,
+  // they are never live across the tile loop's back edge, where a pending
+  // load in a loop-carried register would make the compiler wait for every
+  // outstanding request (next-tile stages and output stores included).
+  float sa_n[T::FM], sw_n = 0.0f;
+  uint32_t b_n = 0;
+  auto load_scalars = [&](const TileAddr& a) {
+    if constexpr (EPI != Epilogue::kRawI32) {
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i) sa_n[i] = sx[min(a.m0 + wm * T::TM + i * 32 + row_in, M - 1)];
+      static_assert(T::BN <= T::kThreads, "one thread per channel of the block");
+      sw_n = 0.0f;
+      b_n = 0;
+      if (tid < T::BN && a.n0 + tid < N) {
+        sw_n = sw[a.n0 + tid];
+        if (bias != nullptr) b_n = bias[a.n0 + tid];
+      }
+    }
+  };
+
   // Split-ring step k: A_k in `ac`, B_k in `bc`, stage k+1 in `an`/`bn1`.
   // After the barrier that frees A_k's and B_k's slots, B_{k+2} and then
   // A_{k+3} are requested into them: at the next barrier only the B part
   // (requested one step earlier) is on the critical path, while A has two
   // steps to land.
   auto step_split = [&](const TileAddr& a, int8_t* ac, int8_t* bc, int8_t* an, int8_t* bn1,
-                        int k, auto interior, auto role, auto fin) __attribute__((always_inline)) {
+                        int k, auto interior, auto role, auto fin, auto loads) __attribute__((always_inline)) {
     constexpr bool kDma = decltype(role)::value;
     constexpr bool kFin = decltype(fin)::value;   // last six steps: requests may reach the next tile
     if constexpr (NB == 1) {
@@ -537,6 +560,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
       wait_lgkmcnt0();
       if constexpr (kDma) wait_vmcnt<DA>();
       barrier();
+      if constexpr (decltype(loads)::value) load_scalars(a);
       if constexpr (kDma && kFin) {
         issue_b_at(a, bc, k + 2, interior);
         issue_a_at(a, ac, k + 3, interior);
@@ -560,6 +584,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     if constexpr (kDma) wait_vmcnt<DA>();   // everything but A_{k+2} (the last request) has landed
     barrier();
     frag_ab(an, bn1, 0, KSUB & 1);
+    if constexpr (decltype(loads)::value) load_scalars(a);
     if constexpr (kDma && kFin) {
       issue_b_at(a, bc, k + 2, interior);
       issue_a_at(a, ac, k + 3, interior);
@@ -584,30 +609,9 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
   // channel scales and biases (fp32) follow the regions, else take the next array
   int8_t* const sb_arr = kEpiOwn || kSbAfter ? reg_a + T::kWaves * kRegion : lds1;
 
-  // Dequant scalars of a tile, requested one tile ahead so that their
-  // latency hides under a K loop: per-token scales of the rows this lane
-  // holds, and (threads below BN) one channel's scale and bias.  Nothing
-  // is done with them until that tile's epilogue (the bias stays in bf16
-  // bits), so no wait for them falls inside this epilogue.
-  float sa_n[T::FM], sw_n = 0.0f;
-  uint32_t b_n = 0;
-  auto load_scalars = [&](const TileAddr& a) {
-    if constexpr (EPI != Epilogue::kRawI32) {
-#pragma unroll
-      for (int i = 0; i < T::FM; ++i) sa_n[i] = sx[min(a.m0 + wm * T::TM + i * 32 + row_in, M - 1)];
-      static_assert(T::BN <= T::kThreads, "one thread per channel of the block");
-      sw_n = 0.0f;
-      b_n = 0;
-      if (tid < T::BN && a.n0 + tid < N) {
-        sw_n = sw[a.n0 + tid];
-        if (bias != nullptr) b_n = bias[a.n0 + tid];
-      }
-    }
-  };
 
   TileAddr cur;
   setup(blockIdx.x, cur);
-  load_scalars(cur);
   if constexpr (T::kSplit) {
     // A slots lds0..lds2 (A_k in slot k%3), B slots lds3, lds4 (B_k in k%2);
     // the slot pattern repeats every 6 stages.
@@ -630,23 +634,29 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
       for (int j = 0; j < T::FN; ++j) acc[i][j] = typename Op::Acc{};
 
     // ---- K loop ----
+    if constexpr (!kEpiOwn) load_scalars(cur);
     if constexpr (T::kSplit) {
       const int KT6 = (KT + 5) / 6 * 6;   // padding stages read as zeros
       // six steps of the ring; the requests they make reach stage kt + 8
       auto kloop = [&](auto role) __attribute__((always_inline)) {
-        auto six = [&](int kt, auto interior, auto fin) __attribute__((always_inline)) {
-          step_split(cur, lds0, lds3, lds1, lds4, kt, interior, role, fin);
-          step_split(cur, lds1, lds4, lds2, lds3, kt + 1, interior, role, fin);
-          step_split(cur, lds2, lds3, lds0, lds4, kt + 2, interior, role, fin);
-          step_split(cur, lds0, lds4, lds1, lds3, kt + 3, interior, role, fin);
-          step_split(cur, lds1, lds3, lds2, lds4, kt + 4, interior, role, fin);
-          step_split(cur, lds2, lds4, lds0, lds3, kt + 5, interior, role, fin);
+        // `last`: the tile's last six steps, whose first one requests the
+        // dequant scalars
+        auto six = [&](int kt, auto interior, auto fin, auto last) __attribute__((always_inline)) {
+          constexpr std::false_type no{};
+          step_split(cur, lds0, lds3, lds1, lds4, kt, interior, role, fin, last);
+          step_split(cur, lds1, lds4, lds2, lds3, kt + 1, interior, role, fin, no);
+          step_split(cur, lds2, lds3, lds0, lds4, kt + 2, interior, role, fin, no);
+          step_split(cur, lds0, lds4, lds1, lds3, kt + 3, interior, role, fin, no);
+          step_split(cur, lds1, lds3, lds2, lds4, kt + 4, interior, role, fin, no);
+          step_split(cur, lds2, lds4, lds0, lds3, kt + 5, interior, role, fin, no);
         };
+        constexpr std::true_type last{};
+        constexpr std::false_type not_last{};
         int kt = 0;
         if constexpr (kSplitK)
-          for (; kt < KT6 && (kt + 9) * T::BK <= K; kt += 6) six(kt, kInterior, std::false_type{});
+          for (; kt < KT6 && (kt + 9) * T::BK <= K; kt += 6) six(kt, kInterior, std::false_type{}, not_last);
         if constexpr (kEpiOwn) {
-          for (; kt < KT6 - 6; kt += 6) six(kt, kChecked, std::false_type{});
+          for (; kt < KT6 - 6; kt += 6) six(kt, kChecked, std::false_type{}, not_last);
           if constexpr (decltype(role)::value) {
             kt6_cur = KT6;
             if (t + (int)gridDim.x < ntiles) {
@@ -657,9 +667,12 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
               pre.rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(W), (short)0, 0, kRsrcWord3);
             }
           }
-          six(kt, kChecked, std::true_type{});
+          six(kt, kChecked, std::true_type{}, last);
+          // wavefronts without requests of their own: their scalar loads
+          // (six steps old) are the only ones that may be outstanding
+          if constexpr (!decltype(role)::value) wait_vmcnt<0>();
         } else {
-          for (; kt < KT6; kt += 6) six(kt, kChecked, std::false_type{});
+          for (; kt < KT6; kt += 6) six(kt, kChecked, std::false_type{}, not_last);
         }
       };
       if constexpr (kHalfDma) {
@@ -720,17 +733,14 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
       int e_lane = lane;
       asm volatile("" : "+v"(e_lane));
       const int e_row = e_lane % 32, e_kh = e_lane / 32;
-      // Scales and bias are requested before the next tile's first DMAs so
-      // that their waits do not include those DMAs.
+      // byte offset of this lane's 8 channels in its output row of a store
+      const uint32_t y_lane = ((uint32_t)(e_lane / 4) * (uint32_t)ldy + (uint32_t)(e_lane % 4) * 8u) * 2u;
       float sa[T::FM];
 #pragma unroll
       for (int i = 0; i < T::FM; ++i) sa[i] = sa_n[i];
       const float sw_l = sw_n, b_l = bf16_to_float((uint16_t)b_n);
       TileAddr nxt;
-      if (has_next) {
-        setup(t_next, nxt);
-        load_scalars(nxt);
-      }
+      if (has_next) setup(t_next, nxt);
       if constexpr (T::kSplit && !kEpiOwn) {
         if (has_next && dma_wave) {
           issue_a(nxt, lds0, 0, kChecked);
@@ -811,8 +821,9 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
               // the out-of-range offset
 #pragma unroll
               for (int it = 0; it < 2; ++it) {
-                const int r = mb - m0 + it * 16 + e_lane / 4;
-                const uint32_t o = n < N ? (uint32_t)(r * ldy + n) * 2u : kOOB;
+                const uint32_t o_tile = ((uint32_t)(mb - m0 + it * 16) * (uint32_t)ldy + (uint32_t)(n0 + nj)) * 2u;
+                uint32_t o = n < N ? y_lane + o_tile : kOOB;
+                asm volatile("" : "+v"(o));   // one store for all lanes, not one per branch
                 __builtin_amdgcn_raw_buffer_store_b128(v[it], y_rsrc, o, 0, 0);
               }
             } else {
