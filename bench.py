@@ -18,8 +18,12 @@ path the method replaces, a same-shape bf16 torch GEMM, and the GEMM rates
 of the other workloads (768px attention projection and MLP pair, 1024px QKV
 with outlier channels).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--no-cold]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 50] [--no-cpu] [--no-cold]
                     [--no-other] [--copy-calibration]
+
+The default warm-up is long on purpose: from idle the GPU needs about 25 ms
+of continuous load before the step rate settles (the first 20 steps after a
+5-step warm-up run about 8% below the steady rate).
 """
 from __future__ import annotations
 
@@ -49,8 +53,8 @@ GEMM_SOURCE = os.path.join(ROOT, "w8a8_int8_quantized_token_amd", "csrc", "gemm_
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-rows", type=int, default=4096, help="tokens per linear in the CPU sample")
     p.add_argument("--no-cold", action="store_true", help="skip the cold-cache GEMM / quantize timings")
@@ -118,14 +122,13 @@ def gpu_ms(fn, stream, n):
     return float(np.median(ts))
 
 
-def step_loop(layer_calls, stream, steps, warmup=2):
+def step_loop(layer_calls, stream, steps, warmup=10):
     """Run `steps` steps of a path the way the timed step runs the fused one:
     per linear, its launches back to back (layer_calls[i] = list of callables),
-    a HIP event before the first and after each.  Returns (wall ms per step,
-    mean ms of each linear's each launch)."""
+    one chain of HIP events per step (before the first launch and after
+    each).  Returns (wall ms per step, mean ms of each linear's each launch)."""
     nl, nph = len(layer_calls), len(layer_calls[0])
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(nph + 1)] for _ in range(nl)]
-          for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nl * nph + 1)] for _ in range(steps)]
     for _ in range(warmup):
         for calls in layer_calls:
             for c in calls:
@@ -133,15 +136,15 @@ def step_loop(layer_calls, stream, steps, warmup=2):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(steps):
+        ev[k][0].record(stream)
         for i, calls in enumerate(layer_calls):
-            ev[k][i][0].record(stream)
             for j, c in enumerate(calls):
                 c()
-                ev[k][i][j + 1].record(stream)
+                ev[k][i * nph + j + 1].record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) / steps * 1e3
-    ms = np.array([[[ev[k][i][j].elapsed_time(ev[k][i][j + 1]) for j in range(nph)] for i in range(nl)]
-                   for k in range(steps)]).mean(axis=0)
+    ms = np.array([[[ev[k][i * nph + j].elapsed_time(ev[k][i * nph + j + 1]) for j in range(nph)]
+                    for i in range(nl)] for k in range(steps)]).mean(axis=0)
     return wall_ms, ms
 
 
@@ -383,19 +386,20 @@ def main():
     step_ops = WORKLOAD.ops
 
     nl = len(layers)
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-            torch.cuda.Event(enable_timing=True)) for _ in range(nl)] for _ in range(args.steps)]
+    # one chain of events per step: before the first launch and after each
+    # (launch 2i quantizes linear i, launch 2i+1 is its GEMM)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nl + 1)] for _ in range(args.steps)]
 
     def step(events=None):
+        if events is not None:
+            events[0].record(stream)
         for i, L in enumerate(layers):
-            if events is not None:
-                events[i][0].record(stream)
             w8.quantize_act(L["x"], L["xq"], L["xs"])
             if events is not None:
-                events[i][1].record(stream)
+                events[2 * i + 1].record(stream)
             w8.linear(L["xq"], L["xs"], L["wq"], L["ws"], L["b"], y=L["y"])
             if events is not None:
-                events[i][2].record(stream)
+                events[2 * i + 2].record(stream)
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -412,8 +416,9 @@ def main():
     value = step_ops * args.steps / elapsed / 1e12
 
     # per-launch kernel times from the events (the stream the kernels run on)
-    q_ms = np.array([[ev[k][i][0].elapsed_time(ev[k][i][1]) for i in range(nl)] for k in range(args.steps)])
-    g_ms = np.array([[ev[k][i][1].elapsed_time(ev[k][i][2]) for i in range(nl)] for k in range(args.steps)])
+    q_ms = np.array([[ev[k][2 * i].elapsed_time(ev[k][2 * i + 1]) for i in range(nl)] for k in range(args.steps)])
+    g_ms = np.array([[ev[k][2 * i + 1].elapsed_time(ev[k][2 * i + 2]) for i in range(nl)]
+                     for k in range(args.steps)])
     per = []
     for i, L in enumerate(layers):
         s = L["shape"]
