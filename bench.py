@@ -193,6 +193,23 @@ def time_cold(fn, stream, scrub, reps=5):
     return float(np.median(ts))
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_backend() -> str:
+    """torch's BLAS backend for the bf16 comparator (on ROCm "Cublaslt" is hipBLASLt)."""
+    b = str(torch.backends.cuda.preferred_blas_library()).split(".")[-1]
+    return {"Cublaslt": "hipBLASLt", "Cublas": "rocBLAS"}.get(b, b)
+
+
 def cpu_baseline(rows: int) -> dict:
     """The oracle, as it stands, on the first `rows` tokens of each linear."""
     import oracle
@@ -212,6 +229,7 @@ def cpu_baseline(rows: int) -> dict:
         ops += 2 * rows * shape.N * shape.K
     threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
     return {"value": round(ops / elapsed / 1e12, 4), "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"first {rows} of {WORKLOAD.linears[0].M} tokens of each of the 4 linears "
                       f"(full N and K), quantize + int32 GEMM + fp32 dequant + bf16; "
                       f"{ops / 1e9:.1f} G int8 ops in {elapsed:.1f} s"}
@@ -510,7 +528,8 @@ def main():
             "bf16_torch_linear_tops": round(step_ops / bf_total / 1e9, 1),
             "step_ms": round(bf_wall, 4), "speedup_step": round(bf_wall / ms_per_step, 3),
             "speedup_full_linear": round(bf_total / (gemm_total_ms + q_total_ms), 3),
-            "speedup_gemm_only": round(bf_total / gemm_total_ms, 3)},
+            "speedup_gemm_only": round(bf_total / gemm_total_ms, 3),
+            "blas_backend": blas_backend()},
         "per_linear": per,
     }
     if not args.no_cpu:
