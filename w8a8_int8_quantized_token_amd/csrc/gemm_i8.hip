@@ -16,8 +16,9 @@
 // Pipeline: a workgroup owns a BM x BN output tile and walks K in stages of
 // BK bytes (128 for the large tiles).  Stages go straight from global memory
 // into LDS with buffer_load ... lds (no staging registers, no LDS store
-// instructions).  The large tiles use a split ring: three X slots and two W
-// slots, so X is requested two stages ahead and W one; the other tiles use a
+// instructions).  The large tiles use a split ring: three slots for one
+// operand and two for the other, so the first is requested two stages ahead
+// and the second one (int8: W ahead, fp8: X ahead); the other tiles use a
 // ring of S whole stages.  Chunks past K or rows past M/N are requested at
 // an out-of-range buffer offset, which the hardware returns as zeros, so
 // partial tiles need no branches and stages past the end add nothing.
@@ -27,9 +28,10 @@
 // the fragment reads conflict on banks.  The accumulators stay in registers
 // for the whole K loop; int32 never touches HBM on the fused path.
 //
-// Persistence: one workgroup per CU walks its share of the tiles; with the
-// split ring the first stage of its next tile is requested before the
-// epilogue of the current one.
+// Persistence: one workgroup per CU walks its share of the tiles.  On the
+// 256x192 int8 tile the ring's requests past a tile's last stage fetch the
+// next tile's first three stages during the last steps; the other split-ring
+// tiles request the next tile's first stage before the epilogue.
 //
 // Workgroup order: consecutive workgroup ids are dispatched round robin over
 // the 8 XCDs, each with its own L2.  Tiles are remapped so that each XCD gets
@@ -61,9 +63,9 @@ constexpr int kDmaBytes = kWave * 16;    // one wavefront DMA: 64 lanes x 16 B
 constexpr uint32_t kOOB = 0x80000000u;    // buffer offset beyond any tile: reads as zero
 constexpr int kRsrcWord3 = 0x00020000;    // raw buffer, 32-bit data format (gfx9 family)
 
-// S >= 2: ring of S whole stages.  S == 0: split ring -- three X slots and
-// two W slots of BM x BK bytes each, so X is requested two stages ahead and
-// W one (see the main loop).
+// S >= 2: ring of S whole stages.  S == 0: split ring -- three slots of one
+// operand and two of the other, so the first is requested two stages ahead
+// and the second one (see the main loop).
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int S_>
 struct Tile {
   static constexpr int BM = BM_;  // X rows (tokens) per workgroup
@@ -966,7 +968,7 @@ hipError_t launch_t(Epilogue epi, const int8_t* xq, const int8_t* wq, const floa
 }
 
 // Compiled tile configurations.
-using CfgSplit = Tile<256, 256, 128, 2, 4, 0>;   // 256x256, X two stages ahead, W one
+using CfgSplit = Tile<256, 256, 128, 2, 4, 0>;   // 256x256, split ring
 using CfgWhole = Tile<256, 256, 128, 2, 4, 2>;   // 256x256, two whole stages
 using Cfg192 = Tile<256, 192, 128, 4, 2, 0>;     // 256x192, split ring
 using CfgTail = Tile<128, 256, 128, 2, 4, 3>;    // 128x256, three whole stages
