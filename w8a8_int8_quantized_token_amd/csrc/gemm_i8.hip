@@ -546,9 +546,13 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
   // After the barrier that frees A_k's and B_k's slots, B_{k+2} and then
   // A_{k+3} are requested into them: at the next barrier only the B part
   // (requested one step earlier) is on the critical path, while A has two
-  // steps to land.
+  // steps to land.  With `pend_out` the A request is left to the next step,
+  // which makes it (`pend_in`, into slot `ap`) alongside its first K step's
+  // MFMAs; it is still that step's last request before its wait, so the
+  // wait's count is unchanged.
   auto step_split = [&](const TileAddr& a, int8_t* ac, int8_t* bc, int8_t* an, int8_t* bn1,
-                        int k, auto interior, auto role, auto fin, auto loads) __attribute__((always_inline)) {
+                        int k, auto interior, auto role, auto fin, auto loads, auto pend_in, auto pend_out,
+                        int8_t* ap) __attribute__((always_inline)) {
     constexpr bool kDma = decltype(role)::value;
     constexpr bool kFin = decltype(fin)::value;   // last six steps: requests may reach the next tile
     if constexpr (NB == 1) {
@@ -575,8 +579,27 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
       interleave1(role);
       return;
     }
+    {
+      frag_ab(ac, bc, 1, 1);
+      if constexpr (kDma && decltype(pend_in)::value) {
+        // the previous step's A request, spread over this step's first MFMAs
+        if constexpr (kFin) issue_a_at(a, ap, k + 2, interior);
+        else issue_a(a, ap, k + 2, interior);
+      }
+      mfmas(0);
+      if constexpr (kDma && decltype(pend_in)::value) {
+        __builtin_amdgcn_sched_group_barrier(0x100, (T::FM + T::FN) * CPS, 0);
 #pragma unroll
-    for (int s = 0; s + 1 < KSUB; ++s) {
+        for (int q = 0; q < T::FM * T::FN; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int s = 1; s + 1 < KSUB; ++s) {
       frag_ab(ac, bc, s + 1, (s + 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
       mfmas(s & 1);
@@ -589,10 +612,10 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     if constexpr (decltype(loads)::value) load_scalars(a);
     if constexpr (kDma && kFin) {
       issue_b_at(a, bc, k + 2, interior);
-      issue_a_at(a, ac, k + 3, interior);
+      if constexpr (!decltype(pend_out)::value) issue_a_at(a, ac, k + 3, interior);
     } else if constexpr (kDma) {
       issue_b(a, bc, k + 2, interior);
-      issue_a(a, ac, k + 3, interior);
+      if constexpr (!decltype(pend_out)::value) issue_a(a, ac, k + 3, interior);
     }
     mfmas((KSUB - 1) & 1);
     interleave(role);
@@ -644,13 +667,17 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
         // `last`: the tile's last six steps, whose first one requests the
         // dequant scalars
         auto six = [&](int kt, auto interior, auto fin, auto last) __attribute__((always_inline)) {
+          // int8: steps 0-4 of the six leave their A request to the next
+          // step's first K step (`ap` is the slot it goes to), so a step's
+          // requests do not all queue behind one barrier
           constexpr std::false_type no{};
-          step_split(cur, lds0, lds3, lds1, lds4, kt, interior, role, fin, last);
-          step_split(cur, lds1, lds4, lds2, lds3, kt + 1, interior, role, fin, no);
-          step_split(cur, lds2, lds3, lds0, lds4, kt + 2, interior, role, fin, no);
-          step_split(cur, lds0, lds4, lds1, lds3, kt + 3, interior, role, fin, no);
-          step_split(cur, lds1, lds3, lds2, lds4, kt + 4, interior, role, fin, no);
-          step_split(cur, lds2, lds4, lds0, lds3, kt + 5, interior, role, fin, no);
+          constexpr std::integral_constant<bool, !Op::kF8> d{};
+          step_split(cur, lds0, lds3, lds1, lds4, kt, interior, role, fin, last, no, d, lds2);
+          step_split(cur, lds1, lds4, lds2, lds3, kt + 1, interior, role, fin, no, d, d, lds0);
+          step_split(cur, lds2, lds3, lds0, lds4, kt + 2, interior, role, fin, no, d, d, lds1);
+          step_split(cur, lds0, lds4, lds1, lds3, kt + 3, interior, role, fin, no, d, d, lds2);
+          step_split(cur, lds1, lds3, lds2, lds4, kt + 4, interior, role, fin, no, d, d, lds0);
+          step_split(cur, lds2, lds4, lds0, lds3, kt + 5, interior, role, fin, no, d, no, lds1);
         };
         constexpr std::true_type last{};
         constexpr std::false_type not_last{};
