@@ -148,17 +148,33 @@ def step_loop(layer_calls, stream, steps, warmup=10):
     return wall_ms, ms
 
 
+def power_cap_w() -> float | None:
+    """The board's package power limit (`rocm-smi --showmaxpower`), or None."""
+    try:
+        r = subprocess.run(["rocm-smi", "--showmaxpower", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        for card in json.loads(r.stdout).values():
+            for k, v in card.items():
+                if "power" in k.lower():
+                    return float(v)
+    except (OSError, ValueError, AttributeError, subprocess.SubprocessError):
+        pass
+    return None
+
+
 def sample_sclk(step, n_steps: int = 600, samples: int = 4) -> dict | None:
-    """Shader clock while the step loop runs: `n_steps` steps are queued
-    (about half a second of GPU work), then `amd-smi metric --clock` is read
-    `samples` times from a child process; the mean over the XCDs' gfx clocks
-    of each sample is kept.  None if the tool is missing or fails."""
+    """Shader clock and socket power while the step loop runs: `n_steps`
+    steps are queued (about half a second of GPU work), then `amd-smi metric
+    --clock --power` is read `samples` times from a child process; the mean
+    over the XCDs' gfx clocks and the socket power of each sample are kept.
+    None if the tool is missing or fails."""
+    cap = power_cap_w()
     for _ in range(n_steps):
         step()
-    vals = []
+    vals, watts = [], []
     try:
         for _ in range(samples):
-            r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True,
+            r = subprocess.run(["amd-smi", "metric", "--clock", "--power", "--json"], capture_output=True,
                                text=True, timeout=20)
             if r.returncode != 0:
                 break
@@ -168,14 +184,20 @@ def sample_sclk(step, n_steps: int = 600, samples: int = 4) -> dict | None:
             xcd = [v["clk"]["value"] for k, v in clk.items() if k.startswith("gfx_")]
             if xcd:
                 vals.append(sum(xcd) / len(xcd))
-    except (OSError, ValueError, KeyError, IndexError, TypeError, subprocess.SubprocessError):
+            pw = gpus[0].get("power", {}).get("socket_power", {}).get("value")
+            if isinstance(pw, (int, float)):
+                watts.append(float(pw))
+    except (OSError, ValueError, KeyError, IndexError, TypeError, AttributeError,
+            subprocess.SubprocessError):
         pass
     torch.cuda.synchronize()
     if not vals:
         return None
     return {"mhz": [round(v) for v in vals], "median_mhz": round(float(np.median(vals))),
-            "source": "amd-smi metric --clock, mean over the XCDs' gfx clocks, read while "
-                      f"{n_steps} steps run (the tool's instantaneous reading, not an average)"}
+            "socket_w": [round(w) for w in watts], "power_cap_w": cap,
+            "source": "amd-smi metric --clock --power (mean over the XCDs' gfx clocks; socket power), "
+                      f"read while {n_steps} steps run (the tool's instantaneous readings, not averages); "
+                      "rocm-smi --showmaxpower for the cap"}
 
 
 def time_cold(fn, stream, scrub, reps=5):
