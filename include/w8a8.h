@@ -110,7 +110,7 @@ w8a8_status w8a8_gemm_f32_fp8_tile(const uint8_t *xq, const uint8_t *wq, float *
  * Row-wise dequantization back to bf16 (the slow path's first step):
  *   out[r,k] = bf16_rne( fl32( float(q[r,k]) * scale[r] ) )
  * for q int8 [R,K] and scale fp32 [R]; out is bf16 [R,K].
- * Abstract: the production "INT8" forward this work replaces quantizes
+ * Abstract: the shipped int8 forward this work replaces quantizes
  * weights and activations and then immediately dequantizes them to bf16 for a
  * bf16 matrix multiply.  Provided so that path can be measured against the
  * fused GEMM; it is not part of the fused path.  Shape contract as above
@@ -163,8 +163,8 @@ w8a8_status w8a8_gemm_i32(const int8_t *xq, const int8_t *wq, int32_t *acc,
                           int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 /*
- * Per-shape tile selection (the abstract's "autotuned per GEMM shape", here a
- * fixed table chosen from measurements).  w8a8_num_tiles() is the number of
+ * Per-shape tile selection (the abstract tunes its kernel for each GEMM shape;
+ * here a fixed table chosen from measurements).  w8a8_num_tiles() is the number of
  * compiled tile configurations; w8a8_tile_info() describes one (block rows of
  * X, block rows of W, K bytes per stage, threads; any pointer may be NULL);
  * w8a8_select_tile() returns the id w8a8_linear would use for a shape.

@@ -1,8 +1,8 @@
 """The dequantize-to-bf16 path (oracle; test infrastructure only).
 
 The abstract of "Realizing Native INT8 Compute for Diffusion Transformers on
-Consumer GPUs" (arXiv 2606.14598) describes the production "INT8" forward it
-replaces: weights and activations are quantized and then immediately
+Consumer GPUs" (arXiv 2606.14598) describes the shipped int8 forward that the
+fused kernel replaces: weights and activations are quantized and then immediately
 dequantized back to bf16, and a bf16 matrix multiply runs on the result.
 Reading taken for the dequantization: v = bf16(fl32(float(q) * s)), i.e. the
 fp32 product of the code and its row scale, rounded to bf16 (nearest even) —

@@ -1,8 +1,8 @@
 """The dequantize-to-bf16 path, kept as a measured comparator.
 
 The abstract of "Realizing Native INT8 Compute for Diffusion Transformers on
-Consumer GPUs" (arXiv 2606.14598) traces the slowness of the production
-"INT8" forward to this path: activations and weights are quantized to int8
+Consumer GPUs" (arXiv 2606.14598) traces the slowness of the shipped int8
+forward to this path: activations and weights are quantized to int8
 and then immediately dequantized back to bf16 for a bf16 matrix multiply, so
 the int8 matrix units are never used.  ``dequant_bf16_linear`` reproduces it
 on the same stored int8 weights as the fused path: per-token quantization
