@@ -395,7 +395,7 @@ def slow_path(w8, layers, per, stream, steps) -> tuple:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+        print(json.dumps({"error": "bench.py runs on one GPU; --gpus must be 1 "
                           "(the multi-GPU sharding is described in the design notes, not built)"}))
         sys.exit(2)
     if not torch.cuda.is_available():
