@@ -185,6 +185,20 @@ def test_rotated_column_walk(w, M, N, K):
         run_linear_check(w, x, W, b, rows, tile=tile, label=f"rotated walk tile{tile}")
 
 
+@pytest.mark.parametrize("M,N,K,with_bias", [(8192, 3072, 256, False), (8192, 3072, 1040, True)])
+def test_per_tile_scalars(w, M, N, K, with_bias):
+    """Several tiles per workgroup with a short K loop (one or two blocks of
+    six stages), with and without bias: each tile's dequant scalars are
+    requested during its own last stages, so a tile must never see its
+    neighbour's scales or bias."""
+    x = datagen.random_bf16((M, K), seed=K + 17)
+    W = datagen.random_bf16((N, K), seed=K + 19, std=0.02)
+    b = datagen.random_bf16((N,), seed=K + 23, std=0.01) if with_bias else None
+    rows = sample_rows(M, 40, K)
+    for tile in range(w.num_tiles()):
+        run_linear_check(w, x, W, b, rows, tile=tile, label=f"per-tile scalars tile{tile}")
+
+
 def test_special_rows(w):
     """Zero rows give exactly the bias; huge, tiny (subnormal-scale) and
     single-spike rows quantize bit-exactly."""
