@@ -140,7 +140,7 @@ w8a8_status w8a8_linear(const int8_t *xq, const float *x_scale, const int8_t *wq
  * transformer MLP):
  *   y[m,n] = bf16_rne( gelu( fl32 value of w8a8_linear above ) ),
  *   gelu(v) = v * Phi(v) (exact erf definition), evaluated in fp32 with a
- *   relative error below 2e-5 (below 1e-6 where |gelu| > 0.01).
+ *   relative error below 3e-5 (below 1e-5 where |gelu| > 1e-6).
  * Abstract: the per-token x per-channel dequantization and the bias are
  * folded into the GEMM epilogue; the activation that follows the linear is
  * folded in the same way, so the pre-activation never reaches memory.  Not
