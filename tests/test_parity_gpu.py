@@ -237,6 +237,23 @@ def test_extreme_codes_closed_form(w):
     assert np.array_equal(acc, sign * 16129 * K)
 
 
+def test_largest_k_closed_form_every_plan(w):
+    """At the largest K the boundary accepts that is a multiple of 16
+    (133136; the int32 bound is 133144), all +-127 codes give
+    acc = +-16129*K = +-2147350544 exactly on every tile plan: the int32
+    accumulators come within 0.01% of overflow and do not wrap."""
+    K = (w.MAX_K // 16) * 16
+    M, N = 40, 72
+    xq = torch.full((M, K), 127, dtype=torch.int8, device=DEV)
+    xq[1::2] = -127
+    wq = torch.full((N, K), 127, dtype=torch.int8, device=DEV)
+    wq[::3] = -127
+    sign = np.where(np.arange(M)[:, None] % 2 == 1, -1, 1) * np.where(np.arange(N)[None, :] % 3 == 0, -1, 1)
+    for tile in range(w.num_tiles()):
+        acc = w.gemm_i32(xq, wq, tile=tile).cpu().numpy().astype(np.int64)
+        assert np.array_equal(acc, sign * 16129 * K), tile
+
+
 def test_unit_scales_zero_bias_give_bf16_of_acc(w):
     M, N, K = 96, 80, 256
     xq = torch.from_numpy(datagen.random_int8((M, K), 1)).to(DEV)
