@@ -199,6 +199,51 @@ def test_per_tile_scalars(w, M, N, K, with_bias):
         run_linear_check(w, x, W, b, rows, tile=tile, label=f"per-tile scalars tile{tile}")
 
 
+def _pattern_rows(rows: np.ndarray, K: int) -> torch.Tensor:
+    """x[m, k] = ((7m + 13k) mod 251 - 125) / 64, exact in bf16, for the given rows (CPU)."""
+    m = torch.from_numpy(rows.astype(np.int64))[:, None]
+    k = torch.arange(K, dtype=torch.int64)[None, :]
+    return (((7 * m + 13 * k) % 251 - 125).to(torch.float32) / 64).to(torch.bfloat16)
+
+
+def test_operands_beyond_4gib(w):
+    """Activation codes of more than 2^32 bytes (M = 1,050,001 tokens at
+    K = 4096): rows on both sides of the 4 GiB boundary and the ragged last
+    row match the oracle, so no row offset wraps at 32 bits."""
+    M, K, N = 1_050_001, 4096, 80
+    x = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
+    kk = (13 * torch.arange(K, device=DEV, dtype=torch.int32)) % 251
+    for r0 in range(0, M, 1 << 16):
+        r1 = min(M, r0 + (1 << 16))
+        mm = (7 * torch.arange(r0, r1, device=DEV, dtype=torch.int32)) % 251
+        x[r0:r1] = (((mm[:, None] + kk[None, :]) % 251 - 125).to(torch.float32) / 64).to(torch.bfloat16)
+    W = datagen.random_bf16((N, K), seed=4096 + N, std=0.02)
+    b = datagen.random_bf16((N,), seed=4097, std=0.01)
+    xq, xs = w.quantize_act(x)
+    del x
+    wq, ws = w.quantize_weight(W.to(DEV))
+    y = w.linear(xq, xs, wq, ws, b.to(DEV))
+    acc = w.gemm_i32(xq, wq)
+    torch.cuda.synchronize()
+    edge = (1 << 32) // K   # first row past 4 GiB of codes
+    rows = np.unique(np.array([0, 1, 255, 256, edge - 257, edge - 2, edge - 1, edge, edge + 1,
+                               edge + 255, M - 257, M - 2, M - 1]))
+    rows = np.concatenate([rows, np.random.default_rng(7).choice(M, 24, replace=False)])
+    rows = np.unique(rows)
+    ref_xq, ref_xs = quantize_rows_ref(_pattern_rows(rows, K))
+    ref_wq, ref_ws = quantize_rows_ref(W)
+    ridx = torch.from_numpy(rows).to(DEV)
+    check_quant(xq.index_select(0, ridx), xs.index_select(0, ridx), ref_xq, ref_xs)
+    check_quant(wq, ws, ref_wq, ref_ws)
+    ref_acc = int_gemm_ref(ref_xq, ref_wq)
+    assert np.array_equal(acc.index_select(0, ridx).cpu().numpy(), ref_acc)
+    y32 = dequant_ref(ref_acc, ref_xs, ref_ws, b)
+    yb = bf16_bits(y.index_select(0, ridx))
+    assert np.array_equal(yb, f32_to_bf16_bits(y32))
+    del xq, acc, y
+    torch.cuda.empty_cache()
+
+
 def test_special_rows(w):
     """Zero rows give exactly the bias; huge, tiny (subnormal-scale) and
     single-spike rows quantize bit-exactly."""
