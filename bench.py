@@ -21,9 +21,11 @@ with outlier channels).
     python bench.py [--gpus 1] [--steps 100] [--warmup 50] [--no-cpu] [--no-cold]
                     [--no-other] [--copy-calibration]
 
-The default warm-up is long on purpose: from idle the GPU needs about 25 ms
-of continuous load before the step rate settles (the first 20 steps after a
-5-step warm-up run about 8% below the steady rate).
+From idle the GPU needs about 25 ms of continuous load before the step rate
+settles (20 steps after a 5-step warm-up from idle ran about 8% below the
+steady rate), so the comparators and variants run first and the headline
+steps (their own warm-up, then the timed steps) follow on a GPU already
+under load; with --only-step they follow the warm-up alone.
 """
 from __future__ import annotations
 
@@ -162,42 +164,72 @@ def power_cap_w() -> float | None:
     return None
 
 
-def sample_sclk(step, n_steps: int = 600, samples: int = 4) -> dict | None:
-    """Shader clock and socket power while the step loop runs: `n_steps`
-    steps are queued (about half a second of GPU work), then `amd-smi metric
-    --clock --power` is read `samples` times from a child process; the mean
-    over the XCDs' gfx clocks and the socket power of each sample are kept.
-    None if the tool is missing or fails."""
-    cap = power_cap_w()
-    for _ in range(n_steps):
-        step()
-    vals, watts = [], []
+def _smi_sample():
+    """One `amd-smi metric --clock --power` reading: (mean gfx clock over the
+    XCDs in MHz, socket power in W), or None."""
     try:
-        for _ in range(samples):
-            r = subprocess.run(["amd-smi", "metric", "--clock", "--power", "--json"], capture_output=True,
-                               text=True, timeout=20)
-            if r.returncode != 0:
-                break
-            data = json.loads(r.stdout)
-            gpus = data["gpu_data"] if isinstance(data, dict) else data
-            clk = gpus[0]["clock"]
-            xcd = [v["clk"]["value"] for k, v in clk.items() if k.startswith("gfx_")]
-            if xcd:
-                vals.append(sum(xcd) / len(xcd))
-            pw = gpus[0].get("power", {}).get("socket_power", {}).get("value")
-            if isinstance(pw, (int, float)):
-                watts.append(float(pw))
+        r = subprocess.run(["amd-smi", "metric", "--clock", "--power", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        if r.returncode != 0:
+            return None
+        data = json.loads(r.stdout)
+        gpus = data["gpu_data"] if isinstance(data, dict) else data
+        clk = gpus[0]["clock"]
+        xcd = [v["clk"]["value"] for k, v in clk.items() if k.startswith("gfx_")]
+        pw = gpus[0].get("power", {}).get("socket_power", {}).get("value")
+        if not xcd or not isinstance(pw, (int, float)):
+            return None
+        return sum(xcd) / len(xcd), float(pw)
     except (OSError, ValueError, KeyError, IndexError, TypeError, AttributeError,
             subprocess.SubprocessError):
-        pass
-    torch.cuda.synchronize()
-    if not vals:
         return None
-    return {"mhz": [round(v) for v in vals], "median_mhz": round(float(np.median(vals))),
-            "socket_w": [round(w) for w in watts], "power_cap_w": cap,
+
+
+def loaded_samples(samples, t0: float, t1: float, cap: float | None) -> list:
+    """(clock, power) of the readings (time, clock, power) taken between t0
+    and t1 with socket power at or above half the package limit `cap` (any
+    power when the limit is unknown)."""
+    thresh = 0.5 * cap if cap else 0.0
+    return [(c, w) for t, c, w in samples if t0 <= t <= t1 and w >= thresh]
+
+
+def sample_sclk(step, ms_per_step: float, seconds: float = 4.0) -> dict | None:
+    """Shader clock and socket power under the step loop.  A thread reads
+    `amd-smi` over and over while the main thread keeps about `seconds` of
+    steps queued; only readings taken while the load was on (socket power at
+    or above half the package limit, and the last reading before the queue
+    drained) are kept as loaded.  None if the tool is missing or fails."""
+    import threading
+    cap = power_cap_w()
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            v = _smi_sample()
+            if v is None:
+                break
+            samples.append((time.perf_counter(), *v))
+
+    n_steps = max(50, int(seconds * 1e3 / max(ms_per_step, 1e-3)))
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    for _ in range(n_steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stop.set()
+    th.join(timeout=30)
+    if not samples:
+        return None
+    loaded = loaded_samples(samples, t0, t1, cap)
+    return {"loaded_mhz": [round(c) for c, _ in loaded], "loaded_w": [round(w) for _, w in loaded],
+            "median_loaded_mhz": round(float(np.median([c for c, _ in loaded]))) if loaded else None,
+            "all_mhz": [round(c) for _, c, _ in samples], "all_w": [round(w) for _, _, w in samples],
+            "power_cap_w": cap, "load_s": round(t1 - t0, 2), "steps": n_steps,
             "source": "amd-smi metric --clock --power (mean over the XCDs' gfx clocks; socket power), "
-                      f"read while {n_steps} steps run (the tool's instantaneous readings, not averages); "
-                      "rocm-smi --showmaxpower for the cap"}
+                      "polled from a thread while the steps ran; loaded = socket power >= half the "
+                      "package limit (rocm-smi --showmaxpower). Instantaneous readings, not averages."}
 
 
 def time_cold(fn, stream, scrub, reps=5):
@@ -441,6 +473,38 @@ def main():
             if events is not None:
                 events[2 * i + 2].record(stream)
 
+    extras = not args.only_step
+    # ---- comparators and variants first: they also bring the GPU to a
+    # steady loaded state (clocks and power management settle after tens of
+    # ms of continuous load), so the headline steps below are not timed
+    # from an idle GPU ----
+    other = None
+    if extras and not args.no_other:
+        log("other workloads")
+        other = time_other_workloads(w8, dev, stream)
+
+    cold = None
+    per_cold = [dict() for _ in layers]
+    if extras and not args.no_cold:
+        cold = cold_timings(w8, layers, per_cold, stream, dev, step_ops,
+                            sum(3 * L["shape"].M * L["shape"].K + 4 * L["shape"].M for L in layers))
+
+    bf_total = None
+    per_bf = [dict() for _ in layers]
+    if extras:
+        log("bf16 comparator")
+        bf_total, bf_wall = bf16_comparator(layers, per_bf, stream, args.steps)
+
+    slow_total = None
+    if extras:
+        log("dequantize-to-bf16 comparator")
+        slow_total, slow_wall = slow_path(w8, layers, per_bf, stream, args.steps)
+
+    fp8 = None
+    if extras:
+        log("fp8 variant")
+        fp8 = time_fp8_variant(w8, layers, stream, args.steps)
+
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
@@ -475,34 +539,10 @@ def main():
     q_bytes = sum(3 * L["shape"].M * L["shape"].K + 4 * L["shape"].M for L in layers)
     q_total_ms = float(q_ms.mean(axis=0).sum())
 
-    extras = not args.only_step
-    sclk = sample_sclk(step) if extras else None
-    # ---- bf16 comparator: torch F.linear, same shapes, same GPU ----
-    bf_total = None
-    if extras:
-        log("bf16 comparator")
-        bf_total, bf_wall = bf16_comparator(layers, per, stream, args.steps)
-
-    # ---- cold caches: GEMM and quantize with L2 and Infinity Cache flushed ----
-    cold = None
-    if extras and not args.no_cold:
-        cold = cold_timings(w8, layers, per, stream, dev, step_ops, q_bytes)
-
-    # ---- the dequantize-to-bf16 path the method replaces (same int8 weights) ----
-    slow_total = None
-    if extras:
-        log("dequantize-to-bf16 comparator")
-        slow_total, slow_wall = slow_path(w8, layers, per, stream, args.steps)
-
-    fp8 = None
-    if extras:
-        log("fp8 variant")
-        fp8 = time_fp8_variant(w8, layers, stream, args.steps)
-
-    other = None
-    if extras and not args.no_other:
-        log("other workloads")
-        other = time_other_workloads(w8, dev, stream)
+    for p, pc, pb in zip(per, per_cold, per_bf):
+        p.update(pc)
+        p.update(pb)
+    sclk = sample_sclk(step, ms_per_step) if extras else None
 
     traffic = gemm_traffic()
     alg_bytes = sum(L["shape"].M * L["shape"].K + L["shape"].N * L["shape"].K

@@ -50,7 +50,12 @@ typedef enum {
   W8A8_ERR_SHAPE = 2,  /* M, N or K outside the shape contract */
   W8A8_ERR_ALIGN = 3,  /* a pointer breaks the alignment contract */
   W8A8_ERR_LAUNCH = 4, /* the HIP runtime rejected a launch (wrong device, no device, ...) */
-  W8A8_ERR_ARG = 5     /* any other invalid argument (e.g. an unknown tile id) */
+  W8A8_ERR_ARG = 5,    /* any other invalid argument (e.g. an unknown tile id) */
+  /* Not statuses: these two make every int32 value a valid w8a8_status, so
+   * that C++ code may hold and compare any value a C caller passes (without
+   * them a value outside 0..7 is undefined behaviour in C++). */
+  W8A8_STATUS_RANGE_MIN_ = -2147483647 - 1,
+  W8A8_STATUS_RANGE_MAX_ = 2147483647
 } w8a8_status;
 
 /* Static, NUL-terminated description of a status code. */
@@ -85,8 +90,13 @@ w8a8_status w8a8_quantize_act(const uint16_t *x, int64_t M, int64_t K,
  *   quantize:  s = fl32(amax / 448), q = e4m3(fl32(v / s)) (nearest, ties to
  *              even, saturating at +-448); an all-zero row gives s = 0, q = 0.
  *   GEMM:      acc[m,n] = sum_k x[m,k] * w[n,k] accumulated in fp32 on the
- *              matrix cores (exact products; the summation order is the
- *              hardware's, within gamma_K * sum |x w| of the exact sum).
+ *              matrix cores (v_mfma_f32_32x32x64_f8f6f4).  The products are
+ *              exact; each instruction adds a block of 64 of them at the
+ *              hardware's own internal precision and order, which the ISA
+ *              does not document, so the sums are not those of sequential
+ *              fp32 additions and carry no bound of the form
+ *              gamma_K * sum |x w|.  Checked against exact sums to the same
+ *              output tolerance as the int8 path.
  *   linear:    the same epilogue as w8a8_linear on the fp32 accumulators.
  * Same shape, alignment and error contracts as the int8 entry points; the
  * raw entry writes fp32 accumulators.

@@ -29,6 +29,15 @@ def test_step_ops_of_the_dit_block():
     assert bench.WORKLOAD.ops == sum(2 * m * k * n for m, k, n in shapes) == 1855425871872
 
 
+def test_comparators_run_before_the_timed_steps():
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    main = src[src.index("def main():"):]
+    timed = main.index('log(f"timing {args.steps} steps")')
+    for phase in ('log("other workloads")', 'log("bf16 comparator")', 'log("fp8 variant")',
+                  'log("dequantize-to-bf16 comparator")', "cold_timings("):
+        assert main.index(phase) < timed, phase
+
+
 def test_defaults_time_a_steady_state():
     sys_argv = sys.argv
     try:
@@ -69,3 +78,13 @@ def test_cpu_model_parsing(tmp_path, monkeypatch, line):
 
     monkeypatch.setattr("builtins.open", fake_open)
     assert bench.cpu_model() == "Some CPU @ 2.0GHz"
+
+
+def test_loaded_clock_samples_keep_only_readings_under_load():
+    samples = [(0.5, 2405.0, 290.0),    # before the load started
+               (1.2, 1750.0, 1210.0), (1.9, 1690.0, 1390.0),
+               (2.4, 2400.0, 310.0),    # queue momentarily empty
+               (3.5, 1800.0, 1100.0)]   # after the load ended
+    assert bench.loaded_samples(samples, 1.0, 3.0, 1400.0) == [(1750.0, 1210.0), (1690.0, 1390.0)]
+    assert bench.loaded_samples(samples, 1.0, 3.0, None) == [(1750.0, 1210.0), (1690.0, 1390.0),
+                                                              (2400.0, 310.0)]

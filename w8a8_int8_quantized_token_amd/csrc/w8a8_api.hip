@@ -51,7 +51,7 @@ int resolve_tile(int tile, int64_t M, int64_t N, int64_t K) {
 extern "C" {
 
 const char* w8a8_status_str(w8a8_status s) {
-  switch (s) {
+  switch (static_cast<int>(s)) {
     case W8A8_OK: return "ok";
     case W8A8_ERR_NULL: return "a required pointer is NULL";
     case W8A8_ERR_SHAPE: return "shape outside the contract (16 <= K, K % 16 == 0, K <= 133144 for GEMMs, N >= 1, 0 <= M)";
