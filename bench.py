@@ -64,6 +64,9 @@ def parse():
     p.add_argument("--only-step", action="store_true",
                    help="time the step only: no comparators, variants, cold or other workloads "
                         "(for profiler runs, whose GEMM dispatches must be the step's alone)")
+    p.add_argument("--with-ceiling", action="store_true",
+                   help="with --only-step: also run the matrix-core ceiling diagnostic after the "
+                        "steps (a kernel of its own name, for counter runs)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run a plain 1 GiB streaming copy 3 times (the reference kernel "
                         "for scaling HBM byte counters)")
@@ -230,6 +233,27 @@ def sample_sclk(step, ms_per_step: float, seconds: float = 4.0) -> dict | None:
             "source": "amd-smi metric --clock --power (mean over the XCDs' gfx clocks; socket power), "
                       "polled from a thread while the steps ran; loaded = socket power >= half the "
                       "package limit (rocm-smi --showmaxpower). Instantaneous readings, not averages."}
+
+
+def mfma_ceiling(w8, L, stream, iters: int = 4000, launches: int = 5) -> dict:
+    """The matrix cores' rate on this GPU for the GEMM's own inner loop and
+    codes (w8a8_mfma_ceiling on the timed step's QKV activation and weight
+    codes): `launches` back-to-back launches of about 4 ms each under the same
+    sustained load as the steps; the median of the last three."""
+    from w8a8_int8_quantized_token_amd.ops import CEILING_MFMAS_PER_ITER
+    ops = CEILING_MFMAS_PER_ITER * iters * 65536
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(launches + 1)]
+    ev[0].record(stream)
+    for i in range(launches):
+        w8.mfma_ceiling(L["xq"], L["wq"], iters)
+        ev[i + 1].record(stream)
+    ev[-1].synchronize()
+    ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(launches - 3, launches))[1]
+    tops = ops / ms / 1e9
+    return {"tops": round(tops, 1), "frac_of_peak": round(tops / MFMA_INT8_PEAK_TOPS, 4),
+            "kernel": "mfma_ceiling_kernel (the GEMM's K step on one LDS-resident stage, no memory "
+                      "traffic, barriers or epilogue)",
+            "codes": f"{L['shape'].name} activation and weight codes of the timed step"}
 
 
 def time_cold(fn, stream, scrub, reps=5):
@@ -542,6 +566,7 @@ def main():
     for p, pc, pb in zip(per, per_cold, per_bf):
         p.update(pc)
         p.update(pb)
+    ceiling = mfma_ceiling(w8, layers[0], stream) if extras or args.with_ceiling else None
     sclk = sample_sclk(step, ms_per_step) if extras else None
 
     traffic = gemm_traffic()
@@ -552,6 +577,8 @@ def main():
                 "achieved": round(gemm_tops, 1), "peak": MFMA_INT8_PEAK_TOPS, "unit": "TOPS",
                 "frac": round(gemm_tops / MFMA_INT8_PEAK_TOPS, 4), "traffic": traffic,
                 "algorithmic_bytes": alg_bytes,
+                "ceiling": None if ceiling is None else dict(
+                    ceiling, frac_of_ceiling=round(gemm_tops / ceiling["tops"], 4)),
                 "per_launch": "sum of 2MNK over the four GEMM launches / sum of their mean durations; "
                               "traffic and algorithmic_bytes are summed over the same four launches"}
 

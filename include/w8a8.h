@@ -34,6 +34,7 @@
 #ifndef W8A8_H_
 #define W8A8_H_
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -193,6 +194,64 @@ w8a8_status w8a8_linear_tile(const int8_t *xq, const float *x_scale, const int8_
                              int64_t M, int64_t N, int64_t K, int tile, hipStream_t stream);
 w8a8_status w8a8_gemm_i32_tile(const int8_t *xq, const int8_t *wq, int32_t *acc,
                                int64_t M, int64_t N, int64_t K, int tile, hipStream_t stream);
+
+/*
+ * K-split fused linear, for shapes whose output tiles are too few to occupy
+ * every compute unit (few tokens and a long K, e.g. the down-projection of a
+ * transformer MLP over a small batch).  Same result, bit for bit, as
+ * w8a8_linear (or w8a8_linear_gelu when `gelu` is non-zero): the K reduction
+ * of each output tile is cut into `splits` equal ranges, each range's exact
+ * int32 sums are written to the caller's workspace, and a second pass adds
+ * the ranges (exactly, in int32) and applies the same fp32 dequantization,
+ * bias (and GELU) epilogue, rounded to bf16.
+ * Abstract: int8 x int8 -> int32 on the matrix cores, per-token x
+ * per-channel dequantization and bias folded into the epilogue; the pages'
+ * GEMM is tuned per shape, and splitting K is this library's answer for
+ * shapes with few output tiles.
+ *   splits <= 0: chosen by the library's cost model (w8a8_select_splitk);
+ *   splits == 1: the plain fused path, no workspace needed;
+ *   splits > 1: requires N % 8 == 0, K % (16 * splits) == 0 (else
+ *                W8A8_ERR_SHAPE), splits <= 64, y and workspace 16-byte
+ *                aligned, and workspace_bytes >=
+ *                w8a8_linear_splitk_workspace(M, N, splits) (else W8A8_ERR_ARG).
+ *   tile < 0: automatic; else a tile id as for w8a8_linear_tile (its main
+ *   tiles are used; W8A8_ERR_ARG if unknown).
+ * The workspace (device memory the caller owns, splits * M * N int32) is
+ * written and read only by this call's kernels, in stream order; calls that
+ * share a workspace must be ordered on one stream.
+ */
+int w8a8_select_splitk(int64_t M, int64_t N, int64_t K, int *tile);
+size_t w8a8_linear_splitk_workspace(int64_t M, int64_t N, int splits);
+w8a8_status w8a8_linear_splitk(const int8_t *xq, const float *x_scale, const int8_t *wq,
+                               const float *w_scale, const uint16_t *bias, uint16_t *y,
+                               int64_t M, int64_t N, int64_t K, int splits, int tile, int gelu,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Diagnostic: the throughput ceiling of w8a8_linear's inner loop on this GPU,
+ * on the caller's codes.  The int8 matrix cores run at a power-limited clock
+ * that depends on the operand values, so the GEMM's rate is best read against
+ * what the same instructions sustain on the same data.  This runs the GEMM's
+ * K step exactly (the 256x192 tile's eight wavefronts, fragment reads from
+ * LDS one K step ahead of the int8 MFMAs) on one 128-byte K stage of xq
+ * [M,K] and wq [N,K] per workgroup, staged in LDS once and looped over
+ * `iters` times, with no memory traffic, barriers or epilogue in the loop:
+ * 256 workgroups of 512 threads, each 49152 * iters MFMAs of
+ * 32x32x32 int8 (65536 int8 operations each).  Time it with events on
+ * `stream`.
+ * Workgroup g takes rows m0 = (g mod floor(M/256)) * 256 of xq,
+ * n0 = (floor(g / floor(M/256)) mod floor(N/192)) * 192 of wq and the K stage
+ * k0 = (g mod floor(K/128)) * 128; its eight wavefronts write the sums of
+ * their int32 accumulators to sink[g*8 .. g*8+7] (int64, device memory,
+ * 2048 entries), which add up to iters * sum over k in the stage of
+ * (sum of xq[m0..m0+255, k]) * (sum of wq[n0..n0+191, k]).
+ * Requires 256 <= M, 192 <= N, 128 <= K <= W8A8_MAX_K, K % 16 == 0 and
+ * 1 <= iters <= 2^40; xq, wq 16-byte and sink 8-byte aligned.  Not part of
+ * the fused path; it exists so measurements can be put against the chip's
+ * power-limited matrix-core rate.
+ */
+w8a8_status w8a8_mfma_ceiling(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64_t K,
+                              int64_t iters, int64_t *sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -16,10 +16,9 @@ Readings taken (the pages give no fp8 recipe):
   * the accumulation is exact here (fp64: every e4m3 x e4m3 product and every
     partial sum of K <= 133144 of them is representable).  A sequential fp32
     sum is within gamma_K * sum_k |x_k w_k| (gamma_K = K u / (1 - K u),
-    u = 2^-24) of it (fp32_sum_bound).  A device may sum in another order or
-    at another internal precision; its result is compared with these exact
-    sums under the output tolerance of the fused linear, not under a bound
-    of this module.
+    u = 2^-24) of it (fp32_sum_bound).  A device that sums blocks of products
+    at an internal precision below fp32 is held to fp8_block_sum_bound, which
+    states its reading of that arithmetic.
 """
 from __future__ import annotations
 
@@ -102,6 +101,27 @@ def fp32_sum_bound(cx, cw) -> np.ndarray:
     u = 2.0 ** -24
     gamma = K * u / (1 - K * u)
     return gamma * (np.abs(e4m3_decode(cx)) @ np.abs(e4m3_decode(cw)).T)
+
+
+def fp8_block_sum_bound(cx, cw) -> np.ndarray:
+    """Accumulation error admitted by reading the matrix-core fp8 GEMM as
+    blocks of 64 exact products, each block summed with at least 22
+    significant bits relative to its largest product, and the block sums
+    added in fp32:
+
+      block:  64 terms, each aligned to the largest one's exponent E and
+              truncated below 2^(E-21): < 64 * 2^-21 * 2^E <= 2^-15 max|p|
+              <= 2^-15 * sum_block |p|;
+      blocks: ceil(K/64) fp32 additions, first order
+              <= ceil(K/64) * 2^-24 * sum_k |x_k w_k|.
+
+    Returns E_K[m,n] = (2^-15 + ceil(K/64) * 2^-24) * sum_k |x[m,k] w[n,k]|.
+    Two bits fewer than fp32's 24 is this reading's allowance for an internal
+    adder narrower than fp32; the instruction set does not document the
+    block sum's internal precision."""
+    K = np.asarray(cx).shape[1]
+    rel = 2.0 ** -15 + -(-K // 64) * 2.0 ** -24
+    return rel * (np.abs(e4m3_decode(cx)) @ np.abs(e4m3_decode(cw)).T)
 
 
 def w8a8_fp8_linear_ref(x, w, bias=None) -> dict:

@@ -139,6 +139,19 @@ int main() {
         }
       }
 
+  // matrix-core ceiling diagnostic: validation only
+  int64_t* sk = p<int64_t>();
+  EXPECT(w8a8_mfma_ceiling(q, q, 255, 192, 128, 1, sk, nullptr), W8A8_ERR_SHAPE);
+  EXPECT(w8a8_mfma_ceiling(q, q, 256, 191, 128, 1, sk, nullptr), W8A8_ERR_SHAPE);
+  EXPECT(w8a8_mfma_ceiling(q, q, 256, 192, 112, 1, sk, nullptr), W8A8_ERR_SHAPE);
+  EXPECT(w8a8_mfma_ceiling(q, q, 256, 192, 136, 1, sk, nullptr), W8A8_ERR_SHAPE);
+  EXPECT(w8a8_mfma_ceiling(q, q, 256, 192, 128, 0, sk, nullptr), W8A8_ERR_ARG);
+  EXPECT(w8a8_mfma_ceiling(q, q, 256, 192, 128, (int64_t(1) << 40) + 1, sk, nullptr), W8A8_ERR_ARG);
+  EXPECT(w8a8_mfma_ceiling(nullptr, q, 256, 192, 128, 1, sk, nullptr), W8A8_ERR_NULL);
+  EXPECT(w8a8_mfma_ceiling(q, q, 256, 192, 128, 1, nullptr, nullptr), W8A8_ERR_NULL);
+  EXPECT(w8a8_mfma_ceiling(p<int8_t>(8), q, 256, 192, 128, 1, sk, nullptr), W8A8_ERR_ALIGN);
+  EXPECT(w8a8_mfma_ceiling(q, q, 256, 192, 128, 1, p<int64_t>(4), nullptr), W8A8_ERR_ALIGN);
+
   if (failures) {
     std::fprintf(stderr, "%d check(s) failed\n", failures);
     return 1;

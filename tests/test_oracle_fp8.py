@@ -9,8 +9,8 @@ from fractions import Fraction
 import numpy as np
 import torch
 
-from oracle.fp8 import (e4m3_decode, e4m3_encode, e4m3_round, fp32_sum_bound, fp8_gemm_ref,
-                        quantize_rows_fp8_ref, w8a8_fp8_linear_ref)
+from oracle.fp8 import (e4m3_decode, e4m3_encode, e4m3_round, fp32_sum_bound, fp8_block_sum_bound,
+                        fp8_gemm_ref, quantize_rows_fp8_ref, w8a8_fp8_linear_ref)
 
 
 def _all_codes():
@@ -121,3 +121,69 @@ def test_linear_whole_path():
     ref = x.double().numpy() @ w.double().numpy().T + b.double().numpy()
     # e4m3 keeps 3 mantissa bits: the product error is a few percent of the scale
     assert np.max(np.abs(r["y32"] - ref)) < 0.1 * np.max(np.abs(ref))
+
+
+def _aligned_block_gemm(cx, cw, bits: int) -> np.ndarray:
+    """Model of a block-summing fp8 unit, computed exactly: per block of 64
+    products (exact), every product truncated toward zero below
+    2^(E - bits + 1) where 2^E <= max|p| < 2^(E+1), the truncated terms summed
+    exactly and rounded to fp32, and the block sums added in fp32 in order."""
+    x, w = e4m3_decode(cx), e4m3_decode(cw)
+    M, K = x.shape
+    N = w.shape[0]
+    out = np.zeros((M, N), dtype=np.float32)
+    for m in range(M):
+        for n in range(N):
+            acc = np.float32(0)
+            for k0 in range(0, K, 64):
+                p = [Fraction(float(a)) * Fraction(float(b)) for a, b in zip(x[m, k0:k0 + 64], w[n, k0:k0 + 64])]
+                big = max(abs(v) for v in p)
+                if big == 0:
+                    continue
+                e = 0
+                while Fraction(2) ** (e + 1) <= big:
+                    e += 1
+                while Fraction(2) ** e > big:
+                    e -= 1
+                q = Fraction(2) ** (e - bits + 1)
+                blk = sum((abs(v) // q) * q * (1 if v >= 0 else -1) for v in p)
+                acc = np.float32(acc + np.float32(float(blk)))
+            out[m, n] = acc
+    return out
+
+
+def test_block_sum_bound_closed_form():
+    # K = 64 products of the same magnitude: (2^-15 + 2^-24) * 64 * |p|
+    cx = e4m3_encode(np.full((1, 64), 2.0))
+    cw = e4m3_encode(np.full((1, 64), -3.0))
+    assert fp8_block_sum_bound(cx, cw)[0, 0] == (2.0 ** -15 + 2.0 ** -24) * 64 * 6.0
+    # K = 130 -> three blocks of the fp32 term
+    cx = e4m3_encode(np.full((2, 130), 0.5))
+    cw = e4m3_encode(np.full((1, 130), 1.0))
+    assert np.all(fp8_block_sum_bound(cx, cw) == (2.0 ** -15 + 3 * 2.0 ** -24) * 65.0)
+
+
+def test_block_sum_bound_covers_a_22_bit_block_adder_and_not_a_20_bit_one():
+    """The bound holds for the model it states (22 significant bits per
+    block), and a 20-bit block adder breaks it on adversarial blocks: one
+    large product and 63 small ones whose low bits the alignment drops."""
+    rng = np.random.default_rng(5)
+    vals = e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    K = 192
+    cx = e4m3_encode(rng.choice(np.concatenate([vals, -vals]), (3, K)))
+    cw = e4m3_encode(rng.choice(np.concatenate([vals, -vals]), (4, K)))
+    # adversarial rows: per block one 448 x 448 product (2^17 <= p < 2^18) and
+    # 63 products 0.125 x 1.875 = 0.234375, just under the 20-bit alignment
+    # step 2^(17 - 19) = 0.25 (all of it dropped), 3.75 steps of the 22-bit one
+    adv_x = np.full(K, 0.125)
+    adv_x[::64] = 448.0
+    adv_w = np.full(K, 1.875)
+    adv_w[::64] = 448.0
+    cx = np.vstack([cx, e4m3_encode(adv_x[None, :])])
+    cw = np.vstack([cw, e4m3_encode(adv_w[None, :])])
+    exact = fp8_gemm_ref(cx, cw)
+    bound = fp8_block_sum_bound(cx, cw)
+    got22 = _aligned_block_gemm(cx, cw, 22).astype(np.float64)
+    assert np.all(np.abs(got22 - exact) <= bound)
+    got20 = _aligned_block_gemm(cx, cw, 20).astype(np.float64)
+    assert np.any(np.abs(got20 - exact) > bound)

@@ -59,8 +59,12 @@ def test_abi_host_code_sanitized(tmp_path):
     flags = ["--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-ffp-contract=off",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", *HOST_SAN,
              "-I", os.path.join(ROOT, "include")]
-    srcs = [os.path.join(CSRC, f) for f in ("w8a8_api.hip", "gemm_i8.hip", "quantize_rows.hip",
-                                             "dequantize_rows.hip")]
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_w8a8_build", os.path.join(ROOT, "w8a8_int8_quantized_token_amd", "build.py"))
+    build = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(build)
+    srcs = [os.path.join(CSRC, f) for f in build.SOURCES]   # every source of the library
     srcs.append(os.path.join(SAN, "abi_check.cpp"))
 
     def compile_one(src):

@@ -46,6 +46,10 @@ def _load() -> ctypes.CDLL:
         "w8a8_gemm_f32_fp8": (st, [p, p, p, i64, i64, i64, p]),
         "w8a8_gemm_f32_fp8_tile": (st, [p, p, p, i64, i64, i64, i32, p]),
         "w8a8_linear_gelu_tile": (st, [p, p, p, p, p, p, i64, i64, i64, i32, p]),
+        "w8a8_mfma_ceiling": (st, [p, p, i64, i64, i64, i64, p, p]),
+        "w8a8_select_splitk": (i32, [i64, i64, i64, p]),
+        "w8a8_linear_splitk_workspace": (ctypes.c_size_t, [i64, i64, i32]),
+        "w8a8_linear_splitk": (st, [p, p, p, p, p, p, i64, i64, i64, i32, i32, i32, p, ctypes.c_size_t, p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)

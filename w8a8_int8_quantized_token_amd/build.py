@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libw8a8.so")
-SOURCES = ["quantize_rows.hip", "dequantize_rows.hip", "gemm_i8.hip", "w8a8_api.hip"]
+SOURCES = ["quantize_rows.hip", "dequantize_rows.hip", "gemm_i8.hip", "splitk_reduce.hip",
+           "mfma_ceiling.hip", "w8a8_api.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

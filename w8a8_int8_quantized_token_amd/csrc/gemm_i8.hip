@@ -38,6 +38,7 @@
 // a contiguous range, walked in groups of kGroupM tile rows, so the tiles
 // resident on one XCD share X and W panels in its L2.
 #include "kernels.h"
+#include "epilogue.h"
 
 #include <algorithm>
 #include <type_traits>
@@ -62,6 +63,11 @@ constexpr int kCUs = 256;               // compute units of an MI355X (one workg
 constexpr int kDmaBytes = kWave * 16;    // one wavefront DMA: 64 lanes x 16 B
 constexpr uint32_t kOOB = 0x80000000u;    // buffer offset beyond any tile: reads as zero
 constexpr int kRsrcWord3 = 0x00020000;    // raw buffer, 32-bit data format (gfx9 family)
+// Cache policy of the output stores: non-temporal (the NT bit of gfx94x/gfx950
+// buffer instructions).  Y is written once and not read again by this kernel;
+// streaming it keeps the operand panels in L2 and leaves fewer dirty lines for
+// the kernel-end write-back (measured: DiT block GEMMs +2.6%, bit-identical).
+constexpr int kStoreNT = 2;
 
 // S >= 2: ring of S whole stages.  S == 0: split ring -- three slots of one
 // operand and two of the other, so the first is requested two stages ahead
@@ -124,35 +130,6 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, int8_t* lds, uin
 
 __device__ __forceinline__ float bf16_to_float(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
-}
-
-// y = fl32(fl32(fl32(acc) * sa) * sw) + b), each step rounded on its own
-// (the int32 accumulator is converted to fp32 with round to nearest even).
-__device__ __forceinline__ float dequant(float acc, float sa, float sw, float b) {
-  return __fadd_rn(__fmul_rn(__fmul_rn(acc, sa), sw), b);
-}
-
-// GELU with the exact (erf) definition, gelu(v) = v * Phi(v), where the
-// normal CDF is Phi(v) = 1 - erfc(v/sqrt2)/2 for v >= 0 and erfc(|v|/sqrt2)/2
-// below.  erfc(z), z >= 0, takes the form of the "erfcc" routine of Numerical
-// Recipes (2nd ed., section 6.2): t = 1/(1 + z/2), erfc = t * exp(-z^2 + P(t)),
-// with our own degree-5 P (gelu_fit.py beside this file: a near-minimax fit of
-// ln(erfc(z)/t) + z^2 on z in [0, 10]; |P - that| < 7.9e-6 evaluated in fp32,
-// so erfc's relative error is below 8e-6).  With the exp argument's rounding
-// (about z^2 * 2^-24) and the hardware reciprocal's 1-ulp error the GELU's
-// relative error stays near 1e-5 -- far below the bf16 rounding of the stored
-// result.  Branch-free: one reciprocal, one exp.
-__device__ __forceinline__ float gelu(float v) {
-  const float z = fabsf(v) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, z, 1.0f));   // v_rcp_f32 (1 ulp)
-  float p = 0.22880949f;
-  p = fmaf(p, t, -0.7092441f);
-  p = fmaf(p, t, 0.47454774f);
-  p = fmaf(p, t, 0.25441802f);
-  p = fmaf(p, t, 1.0180185f);
-  p = fmaf(p, t, -1.2665421f);
-  const float half_erfc = 0.5f * t * __expf(fmaf(-z, z, p));
-  return v * (v >= 0.0f ? 1.0f - half_erfc : half_erfc);
 }
 
 // s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding).
@@ -221,15 +198,27 @@ __device__ __forceinline__ void tile_origin(int t, int tiles_m, int tiles_n, int
   n0 = (in_group / gsize) * bn;
 }
 
-// Persistent kernel: gridDim.x workgroups (at most one per CU) walk the
-// output tiles t = blockIdx.x, blockIdx.x + gridDim.x, ...  With the split
-// ring, the first two requests of a workgroup's next tile are issued before
-// the epilogue of the current one, so the epilogue hides their latency.
+// K split of a launch: the reduction of each output tile is cut into `chunks`
+// equal ranges of K bytes, each its own work item, whose raw int32 sums go to
+// their own output slice (`out_stride` elements apart); the kernel's K is then
+// the length of one range and `ldk` the row length of X and W.  No split:
+// chunks = 1, ldk = K.
+struct KSplit {
+  int ldk;
+  int chunks;
+  int64_t out_stride;
+};
+
+// Persistent kernel: gridDim.x workgroups (at most one per CU) walk the work
+// items t = blockIdx.x, blockIdx.x + gridDim.x, ... (output tile t mod
+// tiles, K range t / tiles).  With the split ring, the first two requests of
+// a workgroup's next item are issued before the epilogue of the current one,
+// so the epilogue hides their latency.
 template <class T, Epilogue EPI, class Op>
 __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     const int8_t* __restrict__ X, const int8_t* __restrict__ W, const float* __restrict__ sx,
     const float* __restrict__ sw, const uint16_t* __restrict__ bias, void* __restrict__ out,
-    int M, int N, int K, int ldy, int tiles_m, int tiles_n, int vec_store) {
+    int M, int N, int K, int ldy, int tiles_m, int tiles_n, int vec_store, KSplit ks) {
   // Split ring, int8: A = W.  In a model the weights arrive cold from HBM at
   // every use while the activation codes were just written by the quantizer
   // (measured: +1.7% on the DiT block step, neutral with warm caches); the
@@ -254,6 +243,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
   int8_t* const ring[4] = {lds0, lds1, lds2, lds3};
 
   const int ntiles = tiles_m * tiles_n;
+  const int nitems = ntiles * ks.chunks;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -295,22 +285,27 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
   constexpr int kStores = 2 * T::FM * T::FN;   // store instructions per wavefront and tile
   const int dma_r = (wave % kDmaWaves) * T::kDmaRows + lane / T::CPR;
   const int col = swz<T::CPR>(dma_r, lane % T::CPR) * 16;   // K byte offset within a stage
-  const uint32_t off0 = (uint32_t)(dma_r * K + col);
-  const uint32_t blk_stride = (uint32_t)(kDmaWaves * T::kDmaRows * K);
+  const uint32_t off0 = (uint32_t)(dma_r * ks.ldk + col);
+  const uint32_t blk_stride = (uint32_t)(kDmaWaves * T::kDmaRows * ks.ldk);
 
-  // Per-tile state (wavefront-uniform): origin and buffer resources over the
-  // tile's rows of X and W.
+  // Per-item state (wavefront-uniform): origin, K range and buffer
+  // resources over the tile's rows of X and W from the range's first byte;
+  // each resource ends with the last valid row's last byte of the range
+  // (rows past M or N read as zeros; bytes of a row past the range are never
+  // requested: the K loop stops at the range's end).
   struct TileAddr {
-    int m0, n0;
+    int m0, n0, c;
     __amdgpu_buffer_rsrc_t rx, rw;
   };
   auto setup = [&](int t, TileAddr& a) {
-    tile_origin(t, tiles_m, tiles_n, T::BM, T::BN, a.m0, a.n0);
+    a.c = t / ntiles;
+    tile_origin(t - a.c * ntiles, tiles_m, tiles_n, T::BM, T::BN, a.m0, a.n0);
     const int rows_x = min(T::BM, M - a.m0), rows_w = min(T::BN, N - a.n0);
-    a.rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(X + (int64_t)a.m0 * K), (short)0,
-                                             rows_x * K, kRsrcWord3);
-    a.rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(W + (int64_t)a.n0 * K), (short)0,
-                                             rows_w * K, kRsrcWord3);
+    const int64_t k0 = (int64_t)a.c * K;
+    a.rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(X + (int64_t)a.m0 * ks.ldk + k0), (short)0,
+                                             (rows_x - 1) * ks.ldk + K, kRsrcWord3);
+    a.rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(W + (int64_t)a.n0 * ks.ldk + k0), (short)0,
+                                             (rows_w - 1) * ks.ldk + K, kRsrcWord3);
   };
   // Request the X (W) part of stage kt of tile `a` into `buf`; chunks at or
   // past K read as zeros.
@@ -648,7 +643,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     frag_ab(lds0, lds3, 0, 0);
   }
 
-  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+  for (int t = blockIdx.x; t < nitems; t += gridDim.x) {
 #pragma unroll
     for (int i = 0; i < T::FM; ++i)
 #pragma unroll
@@ -684,7 +679,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
           for (; kt < KT6 - 6; kt += 6) six(kt, kChecked, std::false_type{}, not_last);
           if constexpr (decltype(role)::value) {
             kt6_cur = KT6;
-            if (t + (int)gridDim.x < ntiles) {
+            if (t + (int)gridDim.x < nitems) {
               setup(t + (int)gridDim.x, pre);
             } else {
               pre.m0 = pre.n0 = 0;
@@ -741,6 +736,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
     }
 
     const int m0 = cur.m0, n0 = cur.n0;
+    [[maybe_unused]] const int c0 = cur.c;
     // output rows of this tile as a buffer range (bf16, ldy apart)
     __amdgpu_buffer_rsrc_t y_rsrc;
     if constexpr (kCountedStores)
@@ -748,7 +744,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
           reinterpret_cast<uint16_t*>(out) + (int64_t)m0 * ldy, (short)0,
           (int)((uint32_t)min(T::BM, M - m0) * (uint32_t)ldy * 2u), kRsrcWord3);
     const int t_next = t + gridDim.x;
-    const bool has_next = t_next < ntiles;
+    const bool has_next = t_next < nitems;
 
     // ---- epilogue: lane holds token m, channels n = base + 8*g + 4*khalf + 0..3 ----
     if constexpr (EPI != Epilogue::kRawI32) {
@@ -849,7 +845,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
                 const uint32_t o_tile = ((uint32_t)(mb - m0 + it * 16) * (uint32_t)ldy + (uint32_t)(n0 + nj)) * 2u;
                 uint32_t o = n < N ? y_lane + o_tile : kOOB;
                 asm volatile("" : "+v"(o));   // one store for all lanes, not one per branch
-                __builtin_amdgcn_raw_buffer_store_b128(v[it], y_rsrc, o, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(v[it], y_rsrc, o, 0, kStoreNT);
               }
             } else {
 #pragma unroll
@@ -890,7 +886,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
       for (int i = 0; i < T::FM; ++i) {
         const int m = m0 + wm * T::TM + i * 32 + row_in;
         if (m >= M) continue;
-        int32_t* crow = reinterpret_cast<int32_t*>(out) + (int64_t)m * ldy;
+        int32_t* crow = reinterpret_cast<int32_t*>(out) + (int64_t)c0 * ks.out_stride + (int64_t)m * ldy;
 #pragma unroll
         for (int j = 0; j < T::FN; ++j) {
 #pragma unroll
@@ -955,16 +951,16 @@ int num_cus() {
 }
 
 // Launch tile configuration T on the sub-problem M x N x K whose output rows
-// are `ldy` elements apart.
+// are `ldy` elements apart (K the length of one K range when `ks` splits it).
 template <class T, class Op>
 hipError_t launch_t(Epilogue epi, const int8_t* xq, const int8_t* wq, const float* sx,
                     const float* sw, const uint16_t* bias, void* out, int64_t M, int64_t N,
-                    int64_t K, int64_t ldy, hipStream_t stream) {
+                    int64_t K, int64_t ldy, hipStream_t stream, KSplit ks) {
   const int tiles_m = (int)((M + T::BM - 1) / T::BM);
   const int tiles_n = (int)((N + T::BN - 1) / T::BN);
   // at most one workgroup per CU (the tiles occupy a whole CU); a multiple
   // of the 8 XCDs so that each workgroup stays on its XCD's tile range
-  const dim3 grid((unsigned)std::min<int64_t>((int64_t)tiles_m * tiles_n, num_cus()));
+  const dim3 grid((unsigned)std::min<int64_t>((int64_t)tiles_m * tiles_n * ks.chunks, num_cus()));
   const dim3 block(T::kThreads);
   const uintptr_t o = reinterpret_cast<uintptr_t>(out);
   if (epi == Epilogue::kBf16ScaleBias) {
@@ -973,19 +969,19 @@ hipError_t launch_t(Epilogue epi, const int8_t* xq, const int8_t* wq, const floa
     const int vec = (ldy % 8 == 0) && (o % 16 == 0) && (int64_t)T::BM * ldy * 2 < (int64_t(1) << 31);
     hipLaunchKernelGGL((gemm_i8_kernel<T, Epilogue::kBf16ScaleBias, Op>), grid, block, 0, stream, xq,
                        wq, sx, sw, bias, out, (int)M, (int)N, (int)K, (int)ldy, tiles_m, tiles_n,
-                       vec);
+                       vec, ks);
   } else if (epi == Epilogue::kBf16GeluScaleBias) {
     // 16-byte stores; the split ring's buffer stores take 32-bit offsets
     // within a tile's rows
     const int vec = (ldy % 8 == 0) && (o % 16 == 0) && (int64_t)T::BM * ldy * 2 < (int64_t(1) << 31);
     hipLaunchKernelGGL((gemm_i8_kernel<T, Epilogue::kBf16GeluScaleBias, Op>), grid, block, 0, stream,
                        xq, wq, sx, sw, bias, out, (int)M, (int)N, (int)K, (int)ldy, tiles_m,
-                       tiles_n, vec);
+                       tiles_n, vec, ks);
   } else {
     const int vec = (ldy % 4 == 0) && (o % 16 == 0);
     hipLaunchKernelGGL((gemm_i8_kernel<T, Epilogue::kRawI32, Op>), grid, block, 0, stream, xq, wq,
                        nullptr, nullptr, nullptr, out, (int)M, (int)N, (int)K, (int)ldy, tiles_m,
-                       tiles_n, vec);
+                       tiles_n, vec, ks);
   }
   return hipGetLastError();
 }
@@ -1010,15 +1006,15 @@ const TileDesc kCfgs[kNumCfg] = {desc<CfgSplit>(), desc<CfgWhole>(), desc<Cfg192
 template <class Op>
 hipError_t launch_cfg(int cfg, Epilogue epi, const int8_t* xq, const int8_t* wq, const float* sx,
                       const float* sw, const uint16_t* bias, void* out, int64_t M, int64_t N,
-                      int64_t K, int64_t ldy, hipStream_t s) {
+                      int64_t K, int64_t ldy, hipStream_t s, KSplit ks) {
   switch (cfg) {
-    case kSplit256: return launch_t<CfgSplit, Op>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
-    case kWhole256: return launch_t<CfgWhole, Op>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
-    case k192: return launch_t<Cfg192, Op>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
-    case kTail128x256: return launch_t<CfgTail, Op>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
-    case k256x128: return launch_t<Cfg256x128, Op>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
-    case k128: return launch_t<Cfg128, Op>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
-    case k64: return launch_t<Cfg64, Op>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s);
+    case kSplit256: return launch_t<CfgSplit, Op>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s, ks);
+    case kWhole256: return launch_t<CfgWhole, Op>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s, ks);
+    case k192: return launch_t<Cfg192, Op>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s, ks);
+    case kTail128x256: return launch_t<CfgTail, Op>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s, ks);
+    case k256x128: return launch_t<Cfg256x128, Op>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s, ks);
+    case k128: return launch_t<Cfg128, Op>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s, ks);
+    case k64: return launch_t<Cfg64, Op>(epi, xq, wq, sx, sw, bias, out, M, N, K, ldy, s, ks);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1122,6 +1118,31 @@ int select_tile(int64_t M, int64_t N, int64_t K) {
   return best;
 }
 
+// ---- K split ----
+// When to split K, from sweeps on MI355X over every plan and range count
+// (M = 256 ... 4096 tokens, N = 3072 / 12288, K = 3072 / 12288): a split pays
+// only when the unsplit launch leaves most compute units idle and K is long.
+// Its cost is the int32 slices (4 bytes per output and range, written by the
+// GEMM and read back by a second pass that also writes the bf16 output) plus
+// one more kernel boundary; on the 768px DiT shapes (200+ tiles) that cost
+// exceeded what balancing the last round saved, e.g. 2304x3072x3072 33.6 us
+// unsplit vs 50+ us in two ranges.  Measured wins: 256x3072x12288 43.4 -> 32.8
+// us (8 ranges), 512x3072x12288 58.1 -> 44.1 us (4 ranges), both on 256x128
+// tiles.  Rule: 256x128 tiles; split only if they number at most 64 and
+// K >= 4096; double the range count while the work items stay within one
+// round of 256 and each range keeps at least 768 bytes of K.
+constexpr int kSplitPlan = 6;   // 256x128 main tiles
+
+int select_splitk(int64_t M, int64_t N, int64_t K, int* tile) {
+  const TileDesc& d = kCfgs[kPlans[kSplitPlan].main];
+  const int64_t tiles = ((M + d.block_m - 1) / d.block_m) * ((N + d.block_n - 1) / d.block_n);
+  int chunks = 1;
+  if (N % 8 == 0 && tiles <= 64 && K >= 4096)
+    while (tiles * chunks * 2 <= kCUs && K % (16 * chunks * 2) == 0 && K / (chunks * 2) >= 768) chunks *= 2;
+  if (tile) *tile = chunks > 1 ? kSplitPlan : select_tile(M, N, K);
+  return chunks;
+}
+
 template <class Op>
 hipError_t launch_plan(int tile, Epilogue epi, const int8_t* xq, const int8_t* wq,
                        const float* sx, const float* sw, const uint16_t* bias, void* out,
@@ -1129,20 +1150,29 @@ hipError_t launch_plan(int tile, Epilogue epi, const int8_t* xq, const int8_t* w
   if (tile < 0 || tile >= kNumPlans) return hipErrorInvalidValue;
   const Plan& p = kPlans[tile];
   const int64_t c = p.tail >= 0 ? main_columns(kCfgs[p.main], M, N) : 0;
-  if (c == 0) return launch_cfg<Op>(p.main, epi, xq, wq, sx, sw, bias, out, M, N, K, N, stream);
+  const KSplit whole{(int)K, 1, 0};
+  if (c == 0) return launch_cfg<Op>(p.main, epi, xq, wq, sx, sw, bias, out, M, N, K, N, stream, whole);
   const int64_t nm = c * kCfgs[p.main].block_n;   // channels done by the main tiles
-  hipError_t e = launch_cfg<Op>(p.main, epi, xq, wq, sx, sw, bias, out, M, nm, K, N, stream);
+  hipError_t e = launch_cfg<Op>(p.main, epi, xq, wq, sx, sw, bias, out, M, nm, K, N, stream, whole);
   if (e != hipSuccess) return e;
   const size_t esz = epi == Epilogue::kRawI32 ? 4 : 2;
   void* out_tail = static_cast<char*>(out) + nm * esz;
   return launch_cfg<Op>(p.tail, epi, xq, wq + nm * K, sx, sw ? sw + nm : nullptr,
-                        bias ? bias + nm : nullptr, out_tail, M, N - nm, K, N, stream);
+                        bias ? bias + nm : nullptr, out_tail, M, N - nm, K, N, stream, whole);
 }
 
 hipError_t launch_gemm(int tile, Epilogue epi, const int8_t* xq, const int8_t* wq,
                        const float* sx, const float* sw, const uint16_t* bias, void* out,
                        int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   return launch_plan<OpI8>(tile, epi, xq, wq, sx, sw, bias, out, M, N, K, stream);
+}
+
+hipError_t launch_gemm_partials(int tile, const int8_t* xq, const int8_t* wq, int32_t* partials,
+                                int64_t M, int64_t N, int64_t K, int chunks, hipStream_t stream) {
+  if (tile < 0 || tile >= kNumPlans || chunks < 1 || K % (16 * chunks) != 0) return hipErrorInvalidValue;
+  const KSplit ks{(int)K, chunks, M * N};
+  return launch_cfg<OpI8>(kPlans[tile].main, Epilogue::kRawI32, xq, wq, nullptr, nullptr, nullptr,
+                          partials, M, N, K / chunks, N, stream, ks);
 }
 
 hipError_t launch_gemm_fp8(int tile, Epilogue epi, const uint8_t* xq, const uint8_t* wq,

@@ -32,6 +32,8 @@ struct TileDesc {
 int num_tiles();
 const TileDesc& tile_desc(int tile);
 int select_tile(int64_t M, int64_t N, int64_t K);
+// K ranges (1 = no split) and plan the split cost model picks for a shape.
+int select_splitk(int64_t M, int64_t N, int64_t K, int* tile);
 
 // kBf16ScaleBias: y = bf16(((acc*sx)*sw)+b); kBf16GeluScaleBias: the same
 // value through GELU before the bf16 rounding; kRawI32: the accumulators.
@@ -44,11 +46,33 @@ hipError_t launch_gemm(int tile, Epilogue epi, const int8_t* xq, const int8_t* w
                        const float* sx, const float* sw, const uint16_t* bias, void* out,
                        int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+// K-split int8 GEMM: the main tiles of plan `tile` over `chunks` equal K
+// ranges (K % (16 * chunks) == 0), each range's raw int32 sums into its own
+// slice partials[c * M * N + m * N + n] (exact; the slices add up to acc).
+hipError_t launch_gemm_partials(int tile, const int8_t* xq, const int8_t* wq, int32_t* partials,
+                                int64_t M, int64_t N, int64_t K, int chunks, hipStream_t stream);
+
+// Sum of the K-split slices plus the bf16 epilogue (kBf16ScaleBias or
+// kBf16GeluScaleBias): y[m,n] from acc = sum_c partials[c][m][n], exactly as
+// the fused GEMM's epilogue evaluates it.  Requires N % 8 == 0.
+hipError_t launch_splitk_reduce(Epilogue epi, const int32_t* partials, int chunks, const float* sx,
+                                const float* sw, const uint16_t* bias, uint16_t* y, int64_t M,
+                                int64_t N, hipStream_t stream);
+
 // The fp8 (e4m3) variant: the same tiles and epilogues on
 // v_mfma_f32_32x32x64_f8f6f4; for kRawI32 `out` receives the fp32
 // accumulators' bits.
 hipError_t launch_gemm_fp8(int tile, Epilogue epi, const uint8_t* xq, const uint8_t* wq,
                            const float* sx, const float* sw, const uint16_t* bias, void* out,
                            int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// Diagnostic: the fused GEMM's K-step (256x192 tile, eight wavefronts) looped
+// `iters` times over one LDS-resident K stage of xq [M,K] and wq [N,K] per
+// workgroup, with no memory traffic in the loop; sink int64
+// [kCeilingWorkgroups * 8] receives each wavefront's accumulator sum.
+// Requires M >= 256, N >= 192, K >= 128 (shapes already validated).
+constexpr int kCeilingWorkgroups = 256;
+hipError_t launch_mfma_ceiling(const int8_t* xq, const int8_t* wq, int64_t M, int64_t N, int64_t K,
+                               int64_t iters, int64_t* sink, hipStream_t stream);
 
 }  // namespace w8a8

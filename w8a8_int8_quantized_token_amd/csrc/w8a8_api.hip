@@ -224,4 +224,61 @@ w8a8_status w8a8_tile_info(int tile, int* block_m, int* block_n, int* block_k, i
 
 int w8a8_select_tile(int64_t M, int64_t N, int64_t K) { return w8a8::select_tile(M, N, K); }
 
+int w8a8_select_splitk(int64_t M, int64_t N, int64_t K, int* tile) {
+  if (check_gemm_shape(M, N, K) != W8A8_OK) return -1;
+  return w8a8::select_splitk(M, N, K, tile);
+}
+
+size_t w8a8_linear_splitk_workspace(int64_t M, int64_t N, int splits) {
+  if (M < 0 || N < 0 || splits < 1) return 0;
+  return splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * sizeof(int32_t) : 0;
+}
+
+w8a8_status w8a8_linear_splitk(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                               const float* w_scale, const uint16_t* bias, uint16_t* y, int64_t M,
+                               int64_t N, int64_t K, int splits, int tile, int gelu,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  w8a8_status st = check_gemm_shape(M, N, K);
+  if (st != W8A8_OK) return st;
+  if (tile >= w8a8::num_tiles() || splits > 64) return W8A8_ERR_ARG;
+  int t = tile;
+  if (splits <= 0) {
+    int auto_tile = 0;
+    splits = w8a8::select_splitk(M, N, K, &auto_tile);
+    if (t < 0) t = auto_tile;
+  }
+  if (t < 0) t = w8a8::select_tile(M, N, K);
+  const w8a8::Epilogue epi = gelu ? w8a8::Epilogue::kBf16GeluScaleBias : w8a8::Epilogue::kBf16ScaleBias;
+  if (splits == 1) return linear_epi(epi, xq, x_scale, wq, w_scale, bias, y, M, N, K, t, stream);
+  if (N % 8 != 0 || K % (16 * splits) != 0) return W8A8_ERR_SHAPE;
+  if (M == 0) return W8A8_OK;
+  if (!x_scale || !w_scale || !workspace) return W8A8_ERR_NULL;
+  st = check_gemm_ptrs(xq, wq, y);
+  if (st != W8A8_OK) return st;
+  if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(y, 16) || !aligned(workspace, 16) ||
+      (bias && !aligned(bias, 2)))
+    return W8A8_ERR_ALIGN;
+  if (workspace_bytes < w8a8_linear_splitk_workspace(M, N, splits)) return W8A8_ERR_ARG;
+  int32_t* part = static_cast<int32_t*>(workspace);
+  if (w8a8::launch_gemm_partials(t, xq, wq, part, M, N, K, splits, stream) != hipSuccess)
+    return W8A8_ERR_LAUNCH;
+  return w8a8::launch_splitk_reduce(epi, part, splits, x_scale, w_scale, bias, y, M, N, stream) ==
+                 hipSuccess
+             ? W8A8_OK
+             : W8A8_ERR_LAUNCH;
+}
+
+w8a8_status w8a8_mfma_ceiling(const int8_t* xq, const int8_t* wq, int64_t M, int64_t N, int64_t K,
+                              int64_t iters, int64_t* sink, hipStream_t stream) {
+  if (M < 256 || M > kMaxRows || N < 192 || N > kMaxRows || K < 128 || K % 16 != 0 ||
+      K > W8A8_MAX_K)
+    return W8A8_ERR_SHAPE;
+  if (iters < 1 || iters > (int64_t(1) << 40)) return W8A8_ERR_ARG;
+  if (!xq || !wq || !sink) return W8A8_ERR_NULL;
+  if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(sink, 8)) return W8A8_ERR_ALIGN;
+  return w8a8::launch_mfma_ceiling(xq, wq, M, N, K, iters, sink, stream) == hipSuccess
+             ? W8A8_OK
+             : W8A8_ERR_LAUNCH;
+}
+
 }  // extern "C"

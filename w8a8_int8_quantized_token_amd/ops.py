@@ -117,6 +117,55 @@ def linear(xq, x_scale, wq, w_scale, bias=None, y=None, tile: int = -1, gelu: bo
     return y
 
 
+def select_splitk(M: int, N: int, K: int) -> tuple[int, int]:
+    """(K ranges, tile id) the library's split cost model picks for a shape."""
+    t = ctypes.c_int(-1)
+    c = lib.w8a8_select_splitk(M, N, K, ctypes.byref(t))
+    if c < 1:
+        raise ValueError("shape outside the GEMM contract")
+    return c, t.value
+
+
+def splitk_workspace_bytes(M: int, N: int, splits: int) -> int:
+    return int(lib.w8a8_linear_splitk_workspace(M, N, splits))
+
+
+def linear_splitk(xq, x_scale, wq, w_scale, bias=None, y=None, splits: int = 0, tile: int = -1,
+                  gelu: bool = False, workspace=None):
+    """The fused W8A8 linear with K split into `splits` ranges (0: the
+    library's choice; 1: no split): the same bits as ``linear``.  The
+    workspace (int32 slices of every range) is allocated here unless given
+    (a uint8 device tensor of at least splitk_workspace_bytes bytes)."""
+    M, N, K = _gemm_args(xq, wq)
+    _need(x_scale, torch.float32, 1, "x_scale")
+    _need(w_scale, torch.float32, 1, "w_scale")
+    if x_scale.shape[0] != M or w_scale.shape[0] != N:
+        raise ValueError("scale lengths do not match M / N")
+    bptr = None
+    if bias is not None:
+        _need(bias, torch.bfloat16, 1, "bias")
+        if bias.shape[0] != N:
+            raise ValueError("bias length does not match N")
+        bptr = bias.data_ptr()
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    _need(y, torch.bfloat16, 2, "y")
+    if tuple(y.shape) != (M, N):
+        raise ValueError("y shape does not match [M,N]")
+    if splits <= 0:
+        splits, auto_tile = select_splitk(M, N, K)
+        tile = auto_tile if tile < 0 else tile
+    need = splitk_workspace_bytes(M, N, splits)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=xq.device)
+    _need(workspace, torch.uint8, 1, "workspace")
+    check(lib.w8a8_linear_splitk(xq.data_ptr(), x_scale.data_ptr(), wq.data_ptr(), w_scale.data_ptr(),
+                                 bptr, y.data_ptr(), M, N, K, splits, tile, int(gelu),
+                                 workspace.data_ptr(), workspace.numel(), _stream(xq)),
+          "w8a8_linear_splitk")
+    return y
+
+
 def gemm_i32(xq, wq, acc=None, tile: int = -1):
     """Raw int32 accumulators acc [M,N] = xq @ wq^T (diagnostic)."""
     M, N, K = _gemm_args(xq, wq)
@@ -179,3 +228,29 @@ def tile_info(tile: int) -> dict:
 
 def select_tile(M: int, N: int, K: int) -> int:
     return lib.w8a8_select_tile(M, N, K)
+
+
+CEILING_WORKGROUPS = 256
+CEILING_MFMAS_PER_ITER = CEILING_WORKGROUPS * 8 * 4 * 6   # workgroups x waves x K steps x MFMAs
+
+
+def mfma_ceiling(xq: torch.Tensor, wq: torch.Tensor, iters: int, sink=None):
+    """Diagnostic: the fused GEMM's K step looped `iters` times on one
+    LDS-resident K stage of xq [M,K] / wq [N,K] per workgroup (no memory
+    traffic in the loop).  Returns sink int64 [256, 8], each wavefront's
+    accumulator sum; the launch does CEILING_MFMAS_PER_ITER * iters int8
+    32x32x32 MFMAs (65536 operations each)."""
+    _need(xq, torch.int8, 2, "xq")
+    _need(wq, torch.int8, 2, "wq")
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError("xq and wq disagree on K")
+    if sink is None:
+        sink = torch.empty((CEILING_WORKGROUPS, 8), dtype=torch.int64, device=xq.device)
+    _need(sink, torch.int64, 2, "sink")
+    if tuple(sink.shape) != (CEILING_WORKGROUPS, 8):
+        raise ValueError("sink must be int64 [256, 8]")
+    check(lib.w8a8_mfma_ceiling(xq.data_ptr(), wq.data_ptr(), M, N, K, iters, sink.data_ptr(),
+                                _stream(xq)), "w8a8_mfma_ceiling")
+    return sink
