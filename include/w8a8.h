@@ -52,6 +52,7 @@ typedef enum {
   W8A8_ERR_ALIGN = 3,  /* a pointer breaks the alignment contract */
   W8A8_ERR_LAUNCH = 4, /* the HIP runtime rejected a launch (wrong device, no device, ...) */
   W8A8_ERR_ARG = 5,    /* any other invalid argument (e.g. an unknown tile id) */
+  W8A8_ERR_SCRATCH = 6, /* more scratch than the no-allocation entry point holds */
   /* Not statuses: these two make every int32 value a valid w8a8_status, so
    * that C++ code may hold and compare any value a C caller passes (without
    * them a value outside 0..7 is undefined behaviour in C++). */
@@ -226,6 +227,29 @@ w8a8_status w8a8_linear_splitk(const int8_t *xq, const float *x_scale, const int
                                const float *w_scale, const uint16_t *bias, uint16_t *y,
                                int64_t M, int64_t N, int64_t K, int splits, int tile, int gelu,
                                void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * w8a8_linear_splitk for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and result without the workspace.  The int32
+ * slices live in a library-owned array of W8A8_NOALLOC_SCRATCH_BYTES (32 MiB)
+ * in each GPU's memory, held from the library's load until the process ends;
+ * its device address is looked up (hipGetSymbolAddress) on the first call on
+ * each device, with that device current.  The call allocates nothing.
+ * Every call on one GPU uses that GPU's one array: calls that may overlap on
+ * one GPU (different streams, or different host threads without ordering)
+ * race on it and must be serialized by the caller; calls in order on one
+ * stream are safe.  No state carries from one call to the next (each slice
+ * element is written before it is read).  A request whose split needs more
+ * than W8A8_NOALLOC_SCRATCH_BYTES (splits * M * N * 4 bytes, splits as
+ * resolved when `splits` <= 0) returns W8A8_ERR_SCRATCH before anything is
+ * launched.  The current device must be the one `stream` belongs to.
+ */
+#define W8A8_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)
+w8a8_status w8a8_linear_splitk_noalloc(const int8_t *xq, const float *x_scale, const int8_t *wq,
+                                       const float *w_scale, const uint16_t *bias, uint16_t *y,
+                                       int64_t M, int64_t N, int64_t K, int splits, int tile,
+                                       int gelu, hipStream_t stream);
 
 /*
  * Diagnostic: the throughput ceiling of w8a8_linear's inner loop on this GPU,

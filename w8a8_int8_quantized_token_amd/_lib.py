@@ -11,7 +11,8 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw8a8.so")
 
 # Status codes of include/w8a8.h
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_LAUNCH, ERR_ARG = range(6)
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_LAUNCH, ERR_ARG, ERR_SCRATCH = range(7)
+NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 MAX_K = 133144
 
 
@@ -50,6 +51,7 @@ def _load() -> ctypes.CDLL:
         "w8a8_select_splitk": (i32, [i64, i64, i64, p]),
         "w8a8_linear_splitk_workspace": (ctypes.c_size_t, [i64, i64, i32]),
         "w8a8_linear_splitk": (st, [p, p, p, p, p, p, i64, i64, i64, i32, i32, i32, p, ctypes.c_size_t, p]),
+        "w8a8_linear_splitk_noalloc": (st, [p, p, p, p, p, p, i64, i64, i64, i32, i32, i32, p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)

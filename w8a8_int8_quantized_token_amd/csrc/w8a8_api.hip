@@ -4,6 +4,8 @@
 #include "../../include/w8a8.h"
 #include "kernels.h"
 
+#include <mutex>
+
 namespace {
 
 constexpr int64_t kMaxRows = int64_t(1) << 26;   // M, N limit (grid size)
@@ -46,6 +48,32 @@ int resolve_tile(int tile, int64_t M, int64_t N, int64_t K) {
   return tile < w8a8::num_tiles() ? tile : -1;
 }
 
+// Scratch of the no-allocation K-split entry point: the int32 slices live in
+// this array, which every GPU the library runs on holds (its own copy) until
+// the process ends.  In host code `scratch` names a host-side stand-in, not
+// the device array: its device address is looked up once per device with
+// hipGetSymbolAddress and only that address is ever passed to kernels.
+static __device__ __align__(256) int8_t scratch[W8A8_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call per device, with that device current).
+w8a8_status scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return W8A8_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return W8A8_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return W8A8_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -58,6 +86,7 @@ const char* w8a8_status_str(w8a8_status s) {
     case W8A8_ERR_ALIGN: return "pointer breaks the alignment contract";
     case W8A8_ERR_LAUNCH: return "HIP kernel launch failed";
     case W8A8_ERR_ARG: return "invalid argument";
+    case W8A8_ERR_SCRATCH: return "the request needs more than the no-allocation entry point's 32 MiB scratch";
   }
   return "unknown status";
 }
@@ -266,6 +295,31 @@ w8a8_status w8a8_linear_splitk(const int8_t* xq, const float* x_scale, const int
                  hipSuccess
              ? W8A8_OK
              : W8A8_ERR_LAUNCH;
+}
+
+w8a8_status w8a8_linear_splitk_noalloc(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                                       const float* w_scale, const uint16_t* bias, uint16_t* y,
+                                       int64_t M, int64_t N, int64_t K, int splits, int tile, int gelu,
+                                       hipStream_t stream) {
+  // the same resolution of `splits` as w8a8_linear_splitk, so the size check
+  // below applies to the split that will run
+  w8a8_status st = check_gemm_shape(M, N, K);
+  if (st != W8A8_OK) return st;
+  if (tile >= w8a8::num_tiles() || splits > 64) return W8A8_ERR_ARG;
+  if (splits <= 0) {
+    int auto_tile = 0;
+    splits = w8a8::select_splitk(M, N, K, &auto_tile);
+    if (tile < 0) tile = auto_tile;
+  }
+  const size_t need = w8a8_linear_splitk_workspace(M, N, splits);
+  if (need > (size_t)W8A8_NOALLOC_SCRATCH_BYTES) return W8A8_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0 && M > 0) {
+    st = scratch_ptr(&ws);
+    if (st != W8A8_OK) return st;
+  }
+  return w8a8_linear_splitk(xq, x_scale, wq, w_scale, bias, y, M, N, K, splits, tile, gelu, ws,
+                            ws ? (size_t)W8A8_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 w8a8_status w8a8_mfma_ceiling(const int8_t* xq, const int8_t* wq, int64_t M, int64_t N, int64_t K,
