@@ -18,21 +18,25 @@ __device__ __forceinline__ float dequant(float acc, float sa, float sw, float b)
 // Recipes (2nd ed., section 6.2): t = 1/(1 + z/2), erfc = t * exp(-z^2 + P(t)),
 // with our own degree-5 P (gelu_fit.py beside this file: a near-minimax fit of
 // ln(erfc(z)/t) + z^2 on z in [0, 10]; |P - that| < 7.9e-6 evaluated in fp32,
-// so erfc's relative error is below 8e-6).  With the exp argument's rounding
-// (about z^2 * 2^-24) and the hardware reciprocal's 1-ulp error the GELU's
-// relative error stays near 1e-5 -- far below the bf16 rounding of the stored
-// result.  Branch-free: one reciprocal, one exp.
+// so erfc's relative error is below 8e-6).  Evaluated as
+//   h = erfc(z)/2 = t * 2^(-log2(e) v^2/2 + Q(t)),  Q = log2(e) P - 1,
+// (z = |v|/sqrt2 folded into the constants, the exponential taken base 2 by
+// the hardware's v_exp_f32, the halving folded into Q's constant term), and
+//   gelu(v) = max(v, 0) - |v h|,
+// which is v - v h for v >= 0 and v h below.  With the exponent's rounding
+// (about v^2 2^-25) and the 1-ulp hardware reciprocal and exp2 the relative
+// error stays near 1e-5 -- far below the bf16 rounding of the stored result.
+// Branch-free: one reciprocal, one exp2, fourteen other operations.
 __device__ __forceinline__ float gelu(float v) {
-  const float z = fabsf(v) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, z, 1.0f));   // v_rcp_f32 (1 ulp)
-  float p = 0.22880949f;
-  p = fmaf(p, t, -0.7092441f);
-  p = fmaf(p, t, 0.47454774f);
-  p = fmaf(p, t, 0.25441802f);
-  p = fmaf(p, t, 1.0180185f);
-  p = fmaf(p, t, -1.2665421f);
-  const float half_erfc = 0.5f * t * __expf(fmaf(-z, z, p));
-  return v * (v >= 0.0f ? 1.0f - half_erfc : half_erfc);
+  const float t = __builtin_amdgcn_rcpf(fmaf(fabsf(v), 0.35355339059327373f, 1.0f));   // v_rcp_f32 (1 ulp)
+  float q = 0.33010232f;
+  q = fmaf(q, t, -1.0232229f);
+  q = fmaf(q, t, 0.6846277f);
+  q = fmaf(q, t, 0.3670476f);
+  q = fmaf(q, t, 1.4686903f);
+  q = fmaf(q, t, -2.827234f);
+  const float h = t * __builtin_amdgcn_exp2f(fmaf(v * -0.72134752044448170f, v, q));   // v_exp_f32
+  return fmaxf(v, 0.0f) - fabsf(v * h);
 }
 
 }  // namespace w8a8

@@ -7,7 +7,9 @@ z in [0, 10] (t in [1/6, 1]; beyond z = 10, erfc(z) < 3e-45 and the fp32
 result is zero either way) by Lawson's iteratively reweighted least squares
 toward the minimax fit, in the Chebyshev basis, then converted to powers of
 t for Horner evaluation.  The relative error of erfc is exp(P - g) - 1, so
-max |P - g| bounds it.
+max |P - g| bounds it.  The kernel evaluates erfc(z)/2 as t * 2^(-log2(e) z^2
++ Q(t)) with Q = log2(e) P - 1 (base-2 exponential, the halving in the
+constant term), so it takes Q's coefficients, printed last.
 
     python gelu_fit.py        # prints the coefficients (highest power first)
 """
@@ -55,3 +57,8 @@ if __name__ == "__main__":
     g = np.log(erfc(z) / t.astype(np.float64)) + z * z
     p32 = np.array([horner_f32(high_first.astype(np.float32), tt) for tt in t], dtype=np.float64)
     print("max |P_fp32 - g|:", f"{np.abs(p32 - g).max():.3e}")
+    q = high_first / np.log(2.0)
+    q[-1] -= 1.0
+    print("coefficients of Q = log2(e) P - 1, highest power first:")
+    for a in q:
+        print(f"  {np.float32(a)!r}")

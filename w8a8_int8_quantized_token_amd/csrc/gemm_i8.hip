@@ -793,70 +793,108 @@ __global__ __launch_bounds__(T::kThreads, 1) void gemm_i8_kernel(
       // and the reads (16 bytes for 4 rows x 4 chunks per quarter-wavefront)
       // fill one 256-byte window.
       auto rsw = [](int r, int c) { return c ^ ((r >> 2) & 3); };
-#pragma unroll
-      for (int j = 0; j < T::FN; ++j) {
-        const int nj = wn * T::TN + j * 32;   // first channel of column tile j in the block
-        f32x4 sv[4], bv[4];
+      f32x4 sv[4], bv[4];
+      // this lane's channel scales and biases of column tile j
+      auto load_sb = [&](int j) {
+        const int nj = wn * T::TN + j * 32;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           sv[g] = *reinterpret_cast<const f32x4*>(s_lds + nj + g * 8 + e_kh * 4);
           bv[g] = *reinterpret_cast<const f32x4*>(b_lds + nj + g * 8 + e_kh * 4);
         }
+      };
+      // 4 bf16 outputs (two packed words) of each run g of output tile (i, j):
+      // channels nj + 8g + 4*khalf + 0..3
+      uint32_t w[4][2];
+      auto pack = [&](int i, int j) {
+        const typename Op::Acc& c = acc[i][j];
+        // the fp32 output value (GELU applied for the gelu epilogue)
+        auto val = [&](int e, float s_w, float b) {
+          const float y = dequant((float)c[e], sa[i], s_w, b);
+          if constexpr (EPI == Epilogue::kBf16GeluScaleBias) return gelu(y);
+          else return y;
+        };
 #pragma unroll
-        for (int i = 0; i < T::FM; ++i) {
-          // 4 bf16 outputs (two packed words) of run g: channels nj + 8g + 4*khalf + 0..3
-          uint32_t w[4][2];
-          const typename Op::Acc& c = acc[i][j];
-          // the fp32 output value (GELU applied for the gelu epilogue)
-          auto val = [&](int e, float s_w, float b) {
-            const float y = dequant((float)c[e], sa[i], s_w, b);
-            if constexpr (EPI == Epilogue::kBf16GeluScaleBias) return gelu(y);
-            else return y;
-          };
+        for (int g = 0; g < 4; ++g) {
+          const bf16x2 lo = __builtin_convertvector(
+              (f32x2{val(g * 4, sv[g][0], bv[g][0]), val(g * 4 + 1, sv[g][1], bv[g][1])}), bf16x2);
+          const bf16x2 hi = __builtin_convertvector(
+              (f32x2{val(g * 4 + 2, sv[g][2], bv[g][2]), val(g * 4 + 3, sv[g][3], bv[g][3])}), bf16x2);
+          w[g][0] = __builtin_bit_cast(uint32_t, lo);
+          w[g][1] = __builtin_bit_cast(uint32_t, hi);
+        }
+      };
+      if (vec_store) {
+        // Software pipeline over the FM x FN output tiles b (column tile j =
+        // b / FM, row tile i = b % FM): tile b's turn-around reads are in
+        // flight while tile b+1 is converted, and tile b+1 is written to the
+        // region once tile b's reads have returned (they feed its stores).
+        constexpr int NB = T::FM * T::FN;
+        auto put = [&]() {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const bf16x2 lo = __builtin_convertvector(
-                (f32x2{val(g * 4, sv[g][0], bv[g][0]), val(g * 4 + 1, sv[g][1], bv[g][1])}), bf16x2);
-            const bf16x2 hi = __builtin_convertvector(
-                (f32x2{val(g * 4 + 2, sv[g][2], bv[g][2]), val(g * 4 + 3, sv[g][3], bv[g][3])}), bf16x2);
-            w[g][0] = __builtin_bit_cast(uint32_t, lo);
-            w[g][1] = __builtin_bit_cast(uint32_t, hi);
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<u32x2*>(region + e_row * 64 + rsw(e_row, g) * 16 +
+                                      8 * (e_kh ^ (e_row >> 4))) = u32x2{w[g][0], w[g][1]};
+        };
+        // The scales and biases of a new column tile are read as soon as the
+        // previous one's last output tile is converted, a whole output tile
+        // ahead of their use -- where the registers allow (up to 6 output
+        // tiles per wavefront; with more, the early copy spills).
+        constexpr bool kSbAhead = NB <= 6;
+        auto pack_next = [&](int x) {
+          if constexpr (!kSbAhead)
+            if (x > 0 && x % T::FM == 0) load_sb(x / T::FM);
+          pack(x % T::FM, x / T::FM);
+          if constexpr (kSbAhead)
+            if (x + 1 < NB && (x + 1) % T::FM == 0) load_sb((x + 1) / T::FM);
+        };
+        load_sb(0);
+        pack_next(0);
+        put();
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int j = b / T::FM, i = b % T::FM;
+          v4i v[2];
+#pragma unroll
+          for (int it = 0; it < 2; ++it) {
+            const int r = it * 16 + e_lane / 4;
+            v[it] = *reinterpret_cast<const v4i*>(region + r * 64 + rsw(r, e_lane % 4) * 16);
           }
+          if (b + 1 < NB) pack_next(b + 1);
+          v[1] = v4i{v[1][2], v[1][3], v[1][0], v[1][1]};   // rows 16..31: halves swapped
+          const int nj = wn * T::TN + j * 32;
           const int mb = m0 + wm * T::TM + i * 32;   // first token of row tile i
-          if (vec_store) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-              *reinterpret_cast<u32x2*>(region + e_row * 64 + rsw(e_row, g) * 16 +
-                                        8 * (e_kh ^ (e_row >> 4))) = u32x2{w[g][0], w[g][1]};
-            v4i v[2];
+          const int n = n0 + nj + (e_lane % 4) * 8;   // this lane's 8 channels when storing
+          if constexpr (kCountedStores) {
+            // exactly two store instructions per 32x32 tile: rows past M
+            // fall outside the tile's buffer range, channels past N go to
+            // the out-of-range offset
 #pragma unroll
             for (int it = 0; it < 2; ++it) {
-              const int r = it * 16 + e_lane / 4;
-              v[it] = *reinterpret_cast<const v4i*>(region + r * 64 + rsw(r, e_lane % 4) * 16);
-            }
-            v[1] = v4i{v[1][2], v[1][3], v[1][0], v[1][1]};   // rows 16..31: halves swapped
-            const int n = n0 + nj + (e_lane % 4) * 8;   // this lane's 8 channels when storing
-            if constexpr (kCountedStores) {
-              // exactly two store instructions per 32x32 tile: rows past M
-              // fall outside the tile's buffer range, channels past N go to
-              // the out-of-range offset
-#pragma unroll
-              for (int it = 0; it < 2; ++it) {
-                const uint32_t o_tile = ((uint32_t)(mb - m0 + it * 16) * (uint32_t)ldy + (uint32_t)(n0 + nj)) * 2u;
-                uint32_t o = n < N ? y_lane + o_tile : kOOB;
-                asm volatile("" : "+v"(o));   // one store for all lanes, not one per branch
-                __builtin_amdgcn_raw_buffer_store_b128(v[it], y_rsrc, o, 0, kStoreNT);
-              }
-            } else {
-#pragma unroll
-              for (int it = 0; it < 2; ++it) {
-                const int m = mb + it * 16 + e_lane / 4;
-                if (m < M && n < N)
-                  *reinterpret_cast<v4i*>(reinterpret_cast<uint16_t*>(out) + (int64_t)m * ldy + n) = v[it];
-              }
+              const uint32_t o_tile = ((uint32_t)(mb - m0 + it * 16) * (uint32_t)ldy + (uint32_t)(n0 + nj)) * 2u;
+              uint32_t o = n < N ? y_lane + o_tile : kOOB;
+              asm volatile("" : "+v"(o));   // one store for all lanes, not one per branch
+              __builtin_amdgcn_raw_buffer_store_b128(v[it], y_rsrc, o, 0, kStoreNT);
             }
           } else {
-            const int m = mb + e_row;
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+              const int m = mb + it * 16 + e_lane / 4;
+              if (m < M && n < N)
+                *reinterpret_cast<v4i*>(reinterpret_cast<uint16_t*>(out) + (int64_t)m * ldy + n) = v[it];
+            }
+          }
+          if (b + 1 < NB) put();
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) {
+          const int nj = wn * T::TN + j * 32;
+          load_sb(j);
+#pragma unroll
+          for (int i = 0; i < T::FM; ++i) {
+            pack(i, j);
+            const int m = m0 + wm * T::TM + i * 32 + e_row;
             if (m < M) {
               uint16_t* yrow = reinterpret_cast<uint16_t*>(out) + (int64_t)m * ldy;
 #pragma unroll
