@@ -11,7 +11,10 @@ HBM.  `value` is int8 TOPS of the whole step: sum of 2*M*N*K over the four
 linears / step time.
 
 Besides the contract fields the JSON line carries the roofline of the
-dominant kernel (the GEMM, timed per launch with HIP events on its stream),
+dominant kernel (the GEMM, timed per launch with HIP events on its stream;
+with the matrix cores' ceiling on the step's own codes, and the fraction of
+the peak scaled to the gfx clock read under load, since the package runs at
+its power limit well below the nominal 2.4 GHz),
 the CPU oracle timed on a bounded sample on the host, the quantize kernel's
 HBM rate, cold-cache timings, the same linears through the dequantize-to-bf16
 path the method replaces, a same-shape bf16 torch GEMM, and the GEMM rates
@@ -47,6 +50,7 @@ import datagen  # noqa: E402
 
 WORKLOAD = datagen.WORKLOADS[4]
 MFMA_INT8_PEAK_TOPS = 5000.0   # MI355X dense int8 matrix peak (5.0 POPS)
+NOMINAL_SCLK_MHZ = 2400.0      # the clock that peak is quoted at
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "gemm_traffic.json")
 GEMM_SOURCE = os.path.join(ROOT, "w8a8_int8_quantized_token_amd", "csrc", "gemm_i8.hip")
@@ -186,6 +190,17 @@ def _smi_sample():
     except (OSError, ValueError, KeyError, IndexError, TypeError, AttributeError,
             subprocess.SubprocessError):
         return None
+
+
+def at_clock(achieved: float, mhz) -> dict | None:
+    """The int8 peak scaled to the gfx clock read under load, and `achieved`
+    (TOPS) as a fraction of it: how much of the matrix cores' rate at the
+    clock the package actually ran at the kernel reaches."""
+    if not mhz:
+        return None
+    peak = MFMA_INT8_PEAK_TOPS * float(mhz) / NOMINAL_SCLK_MHZ
+    return {"mhz": int(mhz), "peak": round(peak, 1), "frac": round(achieved / peak, 4),
+            "note": "5.0 POPS x (median gfx clock read by amd-smi with the step loop running) / 2400 MHz"}
 
 
 def loaded_samples(samples, t0: float, t1: float, cap: float | None) -> list:
@@ -579,6 +594,7 @@ def main():
                 "algorithmic_bytes": alg_bytes,
                 "ceiling": None if ceiling is None else dict(
                     ceiling, frac_of_ceiling=round(gemm_tops / ceiling["tops"], 4)),
+                "at_loaded_clock": at_clock(gemm_tops, (sclk or {}).get("median_loaded_mhz")),
                 "per_launch": "sum of 2MNK over the four GEMM launches / sum of their mean durations; "
                               "traffic and algorithmic_bytes are summed over the same four launches"}
 

@@ -88,3 +88,14 @@ def test_loaded_clock_samples_keep_only_readings_under_load():
     assert bench.loaded_samples(samples, 1.0, 3.0, 1400.0) == [(1750.0, 1210.0), (1690.0, 1390.0)]
     assert bench.loaded_samples(samples, 1.0, 3.0, None) == [(1750.0, 1210.0), (1690.0, 1390.0),
                                                               (2400.0, 310.0)]
+
+
+def test_fraction_at_the_loaded_clock():
+    """The peak scales with the clock: at half the nominal clock the same
+    achieved rate is twice the fraction; no clock reading, no figure."""
+    import bench
+    full = bench.at_clock(2500.0, 2400)
+    half = bench.at_clock(2500.0, 1200)
+    assert full["peak"] == 5000.0 and full["frac"] == 0.5
+    assert half["peak"] == 2500.0 and half["frac"] == 1.0
+    assert bench.at_clock(2500.0, None) is None and bench.at_clock(2500.0, 0) is None
